@@ -1,0 +1,35 @@
+"""Plain, slow, obviously correct CPU reference for the fused attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, tables or helpers); the seeded input generators
+in ``tiled_attention_10_amd.workloads`` are the only thing both sides use, and
+they hold none of the method's arithmetic.
+
+Sources (web pages; cited by title and section):
+
+* [FA3-V3] "FlashAttention（V3）深度解析：从原理到工程实现-Hopper架构下的注意力机制优化革命"
+  (dtcms.com): §2 defines attention, §4.2 the online-softmax merge rule,
+  §4.3 block quantisation, §11 the PyTorch simulation (``standard_attention``,
+  the consumer's online softmax and causal mask).
+* [FA3-card] "FlashAttention-3——利用异步与低精度加速注意力机制" (knowledge card
+  summarising the Together AI blog): "低精度优化：非相干处理" (random-sign
+  Hadamard per head).
+* [FA3-tile] "FlashAttention-3 进阶实录：Tile 级异步流水线与显存带宽榨取实战"
+  (gsyq.cn): §四 keeps the softmax statistics in fp32.
+
+Modules:
+
+* ``attention``  -- fp64 definition of softmax(scale·QKᵀ + mask)·V, sampled
+  rows, LSE, and the two-chunk merge rule (pinned by tests/test_oracle_attention.py).
+* ``e4m3``       -- OCP FP8 E4M3FN decode table and round-to-nearest-even,
+  saturating encoder (pinned against torch's float8_e4m3fn and brute force).
+* ``hadamard``   -- Sylvester Hadamard matrix, fast Walsh–Hadamard transform,
+  random-sign rotation (pinned by orthogonality and invariance tests).
+* ``quant``      -- per-(batch, head, 64-row block) absmax scaling and e4m3
+  codes, with the rounding decisions taken in fp32 (the kernel's precision).
+* ``fp8_attention`` -- fp64 emulation of the fp8 attention path.  PARITY
+  UNPINNED by the pages beyond their qualitative claim: it serves as a loose
+  sanity bound, the criterion being RMSE against the exact fp64 result.
+"""

@@ -1,0 +1,199 @@
+"""Pins for the oracle's E4M3 codes, Hadamard rotation and block quantiser (CPU only).
+
+* E4M3FN decode/encode against torch's float8_e4m3fn (an independent library
+  routine), against the format's defining values, and against brute force
+  nearest-value search over all 256 codes.
+* Hadamard: H·Hᵀ = d·I, scipy's Hadamard matrix, the fast transform equals
+  the explicit product, and the rotation leaves attention unchanged
+  ([FA3-card] "非相干处理": an orthogonal map applied to both Q and K).
+* Quantiser: absmax scaling per (batch, head, 64-row block), saturation,
+  zero blocks, ragged last block, and the rounding error bound of E4M3.
+* FP8 attention emulation: the direction the pages claim (rotation lowers the
+  error on outlier inputs); the emulation itself is "parity unpinned".
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import attention as A
+from oracle import e4m3, hadamard as Hd, quant
+from oracle.fp8_attention import fp8_attention_emul
+from tiled_attention_10_amd import workloads as W
+
+
+def torch_decode_all():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_decode_table_matches_torch():
+    np.testing.assert_array_equal(e4m3.decode_table(), torch_decode_all())
+
+
+def test_defining_values():
+    t = e4m3.decode_table()
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6 and t[0x38] == 1.0
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
+    assert np.isfinite(t[:0x7F]).all() and (np.diff(t[:0x7F]) > 0).all()
+
+
+def _brute_encode(x):
+    t = e4m3.decode_table()
+    fin = np.isfinite(t)
+    out = np.empty(len(x), dtype=np.uint8)
+    for n, v in enumerate(x):
+        a = min(abs(v), 448.0)
+        best = None
+        for c in range(0x7F):
+            dist = abs(t[c] - a)
+            if best is None or dist < best[0] or (dist == best[0] and c % 2 == 0):
+                best = (dist, c)
+        out[n] = best[1] | (0x80 if np.signbit(v) else 0)
+    assert fin.any()
+    return out
+
+
+def _test_values():
+    rng = np.random.default_rng(2)
+    t = e4m3.decode_table()[:0x7F]
+    mids = (t[1:] + t[:-1]) / 2                       # exact ties
+    vals = np.concatenate([
+        rng.standard_normal(3000) * 50, rng.standard_normal(1000) * 1e-2,
+        rng.uniform(-2 ** -8, 2 ** -8, 1000), mids, -mids, t, -t,
+        [0.0, -0.0, 448.0, 449.0, 463.99, 464.0, 465.0, 1e6, -1e6, 2 ** -10, 3 * 2 ** -11],
+    ])
+    return vals.astype(np.float32).astype(np.float64)  # fp32-representable inputs
+
+
+def test_encode_brute_force():
+    x = _test_values()[::3]
+    np.testing.assert_array_equal(e4m3.encode(x), _brute_encode(x))
+
+
+def test_encode_matches_torch_after_clamp():
+    x = _test_values()
+    xt = torch.from_numpy(x.astype(np.float32)).clamp(-448.0, 448.0)
+    want = xt.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(e4m3.encode(x), want)
+
+
+def test_hadamard_matrix():
+    for d in (1, 2, 8, 64, 128):
+        H = Hd.sylvester(d)
+        np.testing.assert_array_equal(H @ H.T, d * np.eye(d))
+        np.testing.assert_array_equal(H, scipy.linalg.hadamard(d))
+
+
+@pytest.mark.parametrize("d", [2, 16, 64, 128])
+def test_fwht_equals_matrix_product(d):
+    x = np.random.default_rng(d).standard_normal((5, 3, d))
+    np.testing.assert_allclose(Hd.fwht(x), x @ scipy.linalg.hadamard(d).T, rtol=0, atol=1e-12)
+    y32 = Hd.fwht(x.astype(np.float32), dtype=np.float32)
+    assert y32.dtype == np.float32
+    np.testing.assert_allclose(y32, x.astype(np.float32).astype(np.float64) @ scipy.linalg.hadamard(d).T,
+                               rtol=0, atol=1e-4 * math.sqrt(d))
+
+
+def test_rotation_is_orthogonal_and_leaves_attention_unchanged():
+    q, k, v = W.random_qkv(21, 1, 96, 4, 2, 128)
+    s = W.rotation_signs(21, 128)
+    qr, kr = Hd.rotate(q, s), Hd.rotate(k, s)
+    np.testing.assert_allclose(np.linalg.norm(qr, axis=-1), np.linalg.norm(q.astype(np.float64), axis=-1),
+                               rtol=1e-13)
+    for causal in (False, True):
+        np.testing.assert_allclose(A.attention(qr, kr, v, None, causal), A.attention(q, k, v, None, causal),
+                                   rtol=0, atol=1e-12)
+    # different signs for Q and K break the invariance: the pin detects a mix-up
+    s2 = -s
+    s2[0] = s[0]
+    assert np.abs(A.attention(Hd.rotate(q, s2), kr, v) - A.attention(q, k, v)).max() > 1e-3
+
+
+def test_rotate_f32_matches_fp64_definition():
+    x = W.to_torch(W.normal(22, 0, (2, 70, 3, 128)), "bf16").float().numpy()
+    s = W.rotation_signs(22, 128)
+    np.testing.assert_allclose(quant.rotate_f32(x, s), Hd.rotate(x, s), rtol=0, atol=2e-5)
+
+
+def test_block_scales_and_codes():
+    x = W.to_torch(W.normal(23, 0, (2, 130, 3, 64)), "bf16").float().numpy()
+    x[1, 64:128, 2] = 0.0                               # an all-zero block
+    codes, scales = quant.quantize(x)
+    assert codes.dtype == np.uint8 and scales.dtype == np.float32
+    assert scales.shape == (2, 3, 3)
+    amax = np.abs(x).reshape(2, 130, 3, 64)
+    for b in range(2):
+        for h in range(3):
+            for blk in range(3):
+                rows = slice(64 * blk, min(130, 64 * blk + 64))
+                a = np.abs(x[b, rows, h]).max()
+                want = np.float32(a) / np.float32(448) if a > 0 else np.float32(1)
+                assert scales[b, h, blk] == want
+                c = codes[b, rows, h] & 0x7F
+                assert c.max() <= 0x7E
+                if a > 0:
+                    assert c.max() == 0x7E                 # the absmax element maps to ±448
+                else:
+                    assert (c == 0).all()
+    assert amax.size
+
+
+def test_dequantisation_error_bound():
+    x = W.to_torch(W.normal(24, 0, (1, 256, 2, 128)), "bf16").float().numpy()
+    codes, scales = quant.quantize(x)
+    deq = quant.dequantize(codes, scales)
+    per_row = np.repeat(scales, 64, axis=2).transpose(0, 2, 1)[..., None].astype(np.float64)
+    # E4M3 round-to-nearest: relative 2^-4 for normals, absolute 2^-10 below 2^-6
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, per_row * 2.0 ** -10) * (1 + 1e-6)
+    assert (np.abs(deq - x) <= bound).all()
+
+
+def test_quantised_rotation_codes_use_fp32_decisions():
+    x = W.to_torch(W.normal(25, 0, (1, 64, 1, 128)), "bf16").float().numpy()
+    s = W.rotation_signs(25, 128)
+    codes, scales = quant.quantize(x, s)
+    y = quant.rotate_f32(x, s)
+    q = (y / scales[0, 0, 0]).astype(np.float32)
+    np.testing.assert_array_equal(codes, e4m3.encode(q))
+
+
+def _c5_like(seed, N=512, H=2):
+    w = W.Workload("c5_small", 900 + seed, 1, N, H, H, 128, "bf16", (False,), outlier_scale=20.0, fp8=True)
+    q, k, v = (W.to_torch(t, "bf16").float().numpy() for t in W.qkv_f32(w))
+    return q, k, v, W.rotation_signs(w.wid, 128)
+
+
+def test_fp8_emulation_error_and_rotation_direction():
+    q, k, v, s = _c5_like(1)
+    exact = A.attention(q, k, v)
+    errs = {}
+    for rot in (False, True):
+        sg = s if rot else None
+        q8, sq = quant.quantize(q, sg)
+        k8, sk = quant.quantize(k, sg)
+        v8, sv = quant.quantize(v, None)
+        o = fp8_attention_emul(q8, k8, v8, sq, sk, sv)
+        errs[rot] = math.sqrt(np.mean((o - exact) ** 2))
+    assert errs[True] < 0.2 * np.std(exact)
+    assert errs[True] <= errs[False], errs
+
+
+def test_fp8_emulation_without_quantisation_error_is_exact():
+    # Inputs that are exact E4M3 values with scale 1 and P quantisation bypassed
+    # by V = 0 rows except one key: the emulation must equal the definition.
+    N, d = 64, 16
+    t = e4m3.decode_table()[:0x7F]
+    rng = np.random.default_rng(3)
+    q = rng.choice(t[t < 2], size=(1, N, 1, d)) * rng.choice([-1, 1], size=(1, N, 1, d))
+    k = rng.choice(t[t < 2], size=(1, N, 1, d)) * rng.choice([-1, 1], size=(1, N, 1, d))
+    v = np.zeros((1, N, 1, d))
+    codes = lambda x: e4m3.encode(x)
+    ones = np.ones((1, 1, 1), dtype=np.float32)
+    o = fp8_attention_emul(codes(q), codes(k), codes(v), ones, ones, ones)
+    np.testing.assert_array_equal(o, np.zeros_like(o))
+    qv = e4m3.decode(codes(q))
+    assert np.array_equal(qv, q)
