@@ -1,0 +1,138 @@
+/*
+ * tattn — tiled fused attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Every tensor is a dense row-major
+ * array laid out [B, N, H, d] (batch, sequence position, head, channel) in
+ * device memory that the caller allocates and owns; the library allocates
+ * nothing and keeps no mutable global state, so calls from several host
+ * threads are safe.  Every call is asynchronous on ``stream`` (a hipStream_t;
+ * NULL means the default stream) and returns before the GPU has finished.
+ *
+ * Return value: TATTN_OK (0) or one of the TATTN_ERR_* codes below.  Argument
+ * checks run on the host before any HIP call, so a rejected call touches
+ * neither the GPU nor the output buffers.  A HIP launch error is returned as
+ * TATTN_ERR_HIP; a device fault after a successful launch surfaces at the
+ * caller's next synchronisation.  tattn_last_error() gives a text detail of
+ * the last failure on the calling thread.  No C++ exception crosses the ABI.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [FA3-V3]   "FlashAttention（V3）深度解析：从原理到工程实现" (dtcms.com)
+ *   [FA3-card] "FlashAttention-3——利用异步与低精度加速注意力机制" (knowledge card
+ *              summarising the Together AI blog post)
+ *   [FA3-tile] "FlashAttention-3 进阶实录：Tile 级异步流水线与显存带宽榨取实战" (gsyq.cn)
+ */
+#ifndef TATTN_H
+#define TATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum {
+  TATTN_F16 = 1,  /* IEEE binary16 */
+  TATTN_BF16 = 2  /* bfloat16 */
+};
+
+/* status codes */
+enum {
+  TATTN_OK = 0,
+  TATTN_ERR_INVALID_ARG = 1, /* null pointer, size < 1, Hq % Hkv != 0, bad scale or flag */
+  TATTN_ERR_UNSUPPORTED = 2, /* head dim not in {64, 128}, unknown dtype */
+  TATTN_ERR_MISALIGNED = 3,  /* a tensor pointer is not 16-byte aligned (lse/scales: 4) */
+  TATTN_ERR_HIP = 4          /* HIP runtime or launch error (see tattn_last_error) */
+};
+
+/*
+ * attn_fwd — O = softmax(scale·Q·Kᵀ + mask)·V for 16-bit inputs.
+ *
+ * Defined by [FA3-V3] §2 (S = QKᵀ, P = softmax(S), O = PV; Q, K, V ∈ R^{N×d}
+ * per head) with §11's 1/sqrt(d) scaling and causal mask (key j is visible to
+ * query i iff j <= i).  Computed tile by tile with the online softmax of
+ * [FA3-V3] §4.2 (running row max m and denominator z, merged as
+ * m = max(m_a, m_b), z = z_a·e^(m_a−m) + z_b·e^(m_b−m)) with fp32 statistics
+ * ([FA3-tile] §四), so the N×N score matrix never reaches memory.
+ *
+ *   q    [B, N, Hq,  d]  dtype           (read)
+ *   k    [B, N, Hkv, d]  dtype           (read)
+ *   v    [B, N, Hkv, d]  dtype           (read)
+ *   o    [B, N, Hq,  d]  dtype           (written; must not alias q, k, v)
+ *   lse  [B, Hq, N]      fp32 or NULL    (written if non-NULL: natural-log
+ *                                         log-sum-exp of each row's scaled,
+ *                                         masked scores)
+ *   B, N, Hq, Hkv >= 1 with Hq % Hkv == 0; query head h reads key/value
+ *   head h / (Hq/Hkv).  d ∈ {64, 128}.  Any N (a partial last tile is masked).
+ *   softmax_scale: finite and > 0 (1/sqrt(d) for the standard definition).
+ *   causal: 0 or 1.  dtype: TATTN_F16 or TATTN_BF16 (output in the same type).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int N, int Hq, int Hkv, int d, float softmax_scale, int causal,
+             int dtype, void* stream);
+
+/*
+ * attn_fwd_fp8 — the same operation on OCP FP8 E4M3FN codes with per-block
+ * scales ([FA3-V3] §4.3: a scale factor per block of the quantised tensor).
+ *
+ * Each tensor x is represented by codes c (uint8, [B, N, H, d]) and fp32 scales
+ * s ([B, H, ceil(N/64)]) with x[b, n, h, :] ≈ e4m3(c[b, n, h, :]) · s[b, h, n/64]
+ * — the output of hadamard_rotate() with a non-NULL scales_out.  Q and K may
+ * have been rotated with the same signs (the product Q·Kᵀ is unchanged by the
+ * rotation); V must not be rotated.  Both products run on FP8 matrix cores with
+ * fp32 accumulation; the scores' scales are applied in fp32; the probabilities
+ * are rounded to E4M3 for the second product after multiplying them by
+ * s_v(block) · 2^8 / max_blocks(s_v) (undone in fp32 in the epilogue), while
+ * the softmax denominator accumulates the unrounded fp32 probabilities.
+ *
+ *   q8, k8, v8              codes as above (read); 16-byte aligned
+ *   q_scale, k_scale, v_scale  fp32 [B, Hq|Hkv, ceil(N/64)], finite and > 0
+ *   o                       [B, N, Hq, d] in out_dtype (TATTN_BF16 or TATTN_F16)
+ *   lse                     as for attn_fwd, or NULL
+ *   other arguments as for attn_fwd (d = 128 only on this path).
+ */
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                 const float* q_scale, const float* k_scale, const float* v_scale,
+                 void* o, float* lse, int B, int N, int Hq, int Hkv, int d,
+                 float softmax_scale, int causal, int out_dtype, void* stream);
+
+/*
+ * hadamard_rotate — random-sign Hadamard rotation of each head's rows,
+ * optionally fused with FP8 block quantisation ([FA3-card] "低精度优化：
+ * 非相干处理": each head's Q and K multiplied by a random orthogonal matrix made
+ * of a Hadamard transform and random signs; [FA3-V3] §4.3: per-block scales).
+ *
+ * For every row r = x[b, n, h, :] of length d:
+ *     y = H_d · (s ⊙ r) / sqrt(d)      if signs != NULL (Sylvester H_d; the
+ *                                      butterfly stages run in fp32 with partner
+ *                                      distance 1, 2, 4, ..., d/2, then one fp32
+ *                                      multiply by fl32(1/sqrt(d)))
+ *     y = r                            if signs == NULL
+ * If scales_out == NULL, y is written to ``y`` in in_dtype (round to nearest
+ * even).  Otherwise, per (b, h, block of 64 consecutive rows):
+ *     scale = absmax(y) / 448            (IEEE fp32 division; 1 for an all-zero block)
+ *     code  = E4M3FN(y · (448/absmax))   (one IEEE fp32 division per block, one
+ *                                         fp32 multiply per element; nearest-even,
+ *                                         saturating at ±448; y · 1 for a zero block)
+ * and ``y`` receives uint8 codes [B, N, H, d], ``scales_out`` fp32
+ * [B, H, ceil(N/64)].
+ *
+ *   x          [B, N, H, d] in_dtype (TATTN_F16 or TATTN_BF16) (read)
+ *   y          output as above; must not alias x
+ *   signs      int8 [d] of +1/-1, or NULL
+ *   d ∈ {64, 128}; B, N, H >= 1.
+ */
+int hadamard_rotate(const void* x, void* y, const int8_t* signs, float* scales_out,
+                    int B, int N, int H, int d, int in_dtype, void* stream);
+
+/* Text for a status code (static storage). */
+const char* tattn_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* tattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TATTN_H */

@@ -6,14 +6,18 @@ is symmetric absmax scaling with no offset.  Blocks are 64 consecutive tokens
 of one (batch, head), all d channels.  Per block:
 
     scale = absmax / 448      (scale = 1 when the block is all zeros)
-    code  = e4m3_rne_saturate(y / scale)
+    code  = e4m3_rne_saturate(y · (448 / absmax))      (y · 1 for a zero block)
+
+The pages do not say how the division by the scale is carried out; the
+reading taken multiplies by the reciprocal 448/absmax computed once per block
+(x ≈ decode(code) · scale still holds to E4M3's rounding).
 
 Where floating point decides the integer code, the decision is taken in fp32,
 the precision the kernel computes in: the optional rotation ([FA3-card]
 "非相干处理"; see ``hadamard``) is the fp32 butterfly in stage order h = 1, 2,
 4, ... followed by one fp32 multiply by fl32(1/sqrt(d)); ``absmax / 448`` and
-``y / scale`` are IEEE fp32 divisions; the fp32 quotient is then rounded to the
-nearest E4M3FN code.  Rows past N inside the last block do not exist and do
+``448 / absmax`` are IEEE fp32 divisions, ``y · (448/absmax)`` one fp32
+multiply; the fp32 product is then rounded to the nearest E4M3FN code.  Rows past N inside the last block do not exist and do
 not enter its absmax.
 """
 from __future__ import annotations
@@ -49,10 +53,13 @@ def quantize(x, signs=None, block=BLOCK):
     """x [B, N, H, d] -> (codes uint8 [B, N, H, d], scales fp32 [B, H, ceil(N/block)])."""
     y = rotate_f32(x, signs) if signs is not None else np.asarray(x, dtype=np.float32)
     amax = block_absmax(y, block)
-    scales = np.where(amax > 0, amax / np.float32(e4m3.E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    m448 = np.float32(e4m3.E4M3_MAX)
+    with np.errstate(divide="ignore"):
+        scales = np.where(amax > 0, amax / m448, np.float32(1.0)).astype(np.float32)
+        inv = np.where(amax > 0, m448 / amax, np.float32(1.0)).astype(np.float32)
     B, N, H, d = y.shape
-    per_row = np.repeat(scales, block, axis=2)[:, :, :N]          # [B, H, N]
-    q = (y / per_row.transpose(0, 2, 1)[..., None]).astype(np.float32)
+    per_row = np.repeat(inv, block, axis=2)[:, :, :N]             # [B, H, N]
+    q = (y * per_row.transpose(0, 2, 1)[..., None]).astype(np.float32)
     return e4m3.encode(q), scales
 
 

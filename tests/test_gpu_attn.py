@@ -1,0 +1,126 @@
+"""GPU parity of attn_fwd (fp16/bf16) against the fp64 CPU oracle, through the C ABI.
+
+Tolerances are the ones the method's target states for inputs ~ N(0,1):
+max |ΔO| <= 2e-3 for fp16 and <= 1e-2 for bf16.  Small shapes are compared
+element by element (several tiles plus ragged tails); the large workloads are
+compared on sampled rows that the oracle computes exactly, in the same launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tiled_attention_10_amd as T
+from oracle import attention as A
+from tiled_attention_10_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp16": 2e-3, "bf16": 1e-2}
+DEV = "cuda:0"
+
+
+def run(q, k, v, causal, scale=None, lse=False):
+    print(f"[attn_fwd] q{tuple(q.shape)} k{tuple(k.shape)} {q.dtype} causal={causal}", flush=True)
+    r = T.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, softmax_scale=scale, return_lse=lse)
+    torch.cuda.synchronize()
+    if lse:
+        return r[0].float().cpu().numpy(), r[1].cpu().numpy()
+    return r.float().cpu().numpy()
+
+
+SMALL = [
+    (1, 1, 1, 1, 64), (1, 3, 2, 1, 128), (1, 64, 1, 1, 128), (2, 127, 4, 2, 64), (1, 128, 2, 2, 128),
+    (1, 129, 2, 2, 128), (2, 333, 8, 8, 64), (1, 1000, 4, 1, 128), (1, 700, 6, 3, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}N{}H{}/{}d{}".format(*s))
+def test_small_shapes_elementwise(shape, causal, dtype):
+    B, N, Hq, Hkv, d = shape
+    q, k, v = (W.to_torch(x, dtype) for x in W.random_qkv(sum(shape), B, N, Hq, Hkv, d))
+    o, lse = run(q, k, v, causal, lse=True)
+    ref, ref_lse = A.attention(q, k, v, None, causal, return_lse=True)
+    err = np.abs(o - ref).max()
+    assert err <= TOL[dtype], err
+    assert np.abs(lse - ref_lse).max() <= 1e-4 * max(1.0, np.abs(ref_lse).max())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_tiny_workload(dtype):
+    w = W.WORKLOADS["tiny_h1_n128_d64"]
+    q, k, v = (W.to_torch(x, dtype) for x in W.qkv_f32(w))
+    o = run(q, k, v, False)
+    # the oracle runs on the same rounded values the GPU receives
+    assert np.abs(o - A.attention(q, k, v)).max() <= TOL[dtype]
+    # and the rounding of the fp32 inputs themselves moves the result by far less than the tolerance
+    q32, k32, v32 = W.qkv_f32(w)
+    assert np.abs(A.attention(q32, k32, v32) - A.attention(q, k, v)).max() < 5 * TOL[dtype]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mha_fp16_full(causal):
+    w = W.WORKLOADS["mha_fp16_b4_h16_n2048"]
+    q, k, v = (W.to_torch(x, "fp16") for x in W.qkv_f32(w))
+    o = run(q, k, v, causal)
+    ref = A.attention(q, k, v, None, causal)
+    assert np.abs(o - ref).max() <= TOL["fp16"]
+
+
+def sample_rows(N, seed, n=160, bm=128):
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, N - 1] + [x for t in range(bm, N, bm * max(1, N // (bm * 16))) for x in (t - 1, t)]
+    return np.unique(np.concatenate([edges, rng.integers(0, N, n)]))
+
+
+@pytest.mark.parametrize("name,causal", [("gqa_bf16_h64kv8_n8192", True), ("gqa_bf16_h64kv8_n8192", False),
+                                         ("long_bf16_h8kv1_n131072", True)])
+def test_large_workloads_sampled_rows(name, causal):
+    w = W.WORKLOADS[name]
+    q, k, v = (W.to_torch(x, "bf16") for x in W.qkv_f32(w))
+    o, lse = run(q, k, v, causal, lse=True)
+    rows = sample_rows(w.N, w.wid, n=96 if w.N > 100000 else 160)
+    heads = list(range(0, w.Hq, max(1, w.Hq // 8)))
+    ref, ref_lse = A.attention_rows(q, k, v, rows, None, causal, heads=heads)
+    err = np.abs(o[:, rows][:, :, heads] - ref).max()
+    print(f"{name} causal={causal}: {len(rows)} rows x {len(heads)} heads, max|dO| = {err:.3e}")
+    assert err <= TOL["bf16"]
+    assert np.abs(lse[:, heads][:, :, rows] - ref_lse).max() <= 1e-3
+    assert np.isfinite(o).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_causal_row0_is_v0_bit_exact(dtype):
+    q, k, v = (W.to_torch(x, dtype) for x in W.random_qkv(31, 2, 300, 4, 2, 128))
+    o = T.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True).cpu()
+    for h in range(4):
+        assert torch.equal(o[:, 0, h], v[:, 0, h // 2])
+
+
+def test_deterministic_and_gqa_equals_repeated_mha():
+    q, k, v = (W.to_torch(x, "bf16").to(DEV) for x in W.random_qkv(32, 1, 777, 8, 2, 128))
+    a = T.attn_fwd(q, k, v, causal=True)
+    b = T.attn_fwd(q, k, v, causal=True)
+    c = T.attn_fwd(q, k.repeat_interleave(4, dim=2).contiguous(), v.repeat_interleave(4, dim=2).contiguous(),
+                   causal=True)
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_scale_argument_is_used():
+    q, k, v = (W.to_torch(x, "fp16") for x in W.random_qkv(33, 1, 200, 2, 2, 64))
+    o = run(q, k, v, False, scale=0.37)
+    assert np.abs(o - A.attention(q, k, v, 0.37)).max() <= TOL["fp16"]
+
+
+def test_binding_rejects_bad_calls():
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        T.attn_fwd(q, q[:, :32].contiguous(), q)
+    with pytest.raises(TypeError):
+        T.attn_fwd(q.float(), q.float(), q.float())
+    q96 = torch.zeros(1, 64, 2, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(T.TattnError) as e:
+        T.attn_fwd(q96, q96, q96)
+    assert e.value.status == 2

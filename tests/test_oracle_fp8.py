@@ -157,7 +157,10 @@ def test_quantised_rotation_codes_use_fp32_decisions():
     s = W.rotation_signs(25, 128)
     codes, scales = quant.quantize(x, s)
     y = quant.rotate_f32(x, s)
-    q = (y / scales[0, 0, 0]).astype(np.float32)
+    amax = np.abs(y).max()
+    assert scales[0, 0, 0] == amax / np.float32(448)
+    q = (y * (np.float32(448) / amax)).astype(np.float32)
+    assert q.dtype == np.float32
     np.testing.assert_array_equal(codes, e4m3.encode(q))
 
 

@@ -1,0 +1,130 @@
+// C ABI of libtattn: argument validation, error reporting and dispatch to the
+// gfx950 kernels.  All checks run on the host before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "tattn.h"
+#include "tattn_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Element counts must stay addressable with 64-bit offsets and the grid with
+// 32-bit workgroup ids.
+bool too_large(long long B, long long N, long long H, long long d) {
+  const long long lim = (long long)1 << 40;
+  return B > lim / N || B * N > lim / H || B * N * H > lim / d;
+}
+
+int check_shape(int B, int N, int Hq, int Hkv, int d) {
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1)
+    return fail(TATTN_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d N=%d Hq=%d Hkv=%d)", B, N, Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(TATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (too_large(B, N, Hq, d > 0 ? d : 1))
+    return fail(TATTN_ERR_INVALID_ARG, "tensor too large (B=%d N=%d H=%d d=%d)", B, N, Hq, d);
+  const long long grid = (long long)((N + 127) / 128) * Hq * B;
+  if (grid > 0x7fffffffLL) return fail(TATTN_ERR_INVALID_ARG, "too many query tiles");
+  return TATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TATTN_OK;
+  return fail(TATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tattn_status_string(int status) {
+  switch (status) {
+    case TATTN_OK: return "ok";
+    case TATTN_ERR_INVALID_ARG: return "invalid argument";
+    case TATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case TATTN_ERR_MISALIGNED: return "misaligned pointer";
+    case TATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* tattn_last_error(void) { return g_last_error; }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N,
+             int Hq, int Hkv, int d, float softmax_scale, int causal, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !o) return fail(TATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (int s = check_shape(B, N, Hq, Hkv, d)) return s;
+  if (d != 64 && d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (dtype != TATTN_F16 && dtype != TATTN_BF16) return fail(TATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(TATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(TATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(TATTN_ERR_MISALIGNED, "q, k, v, o must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(TATTN_ERR_MISALIGNED, "lse must be 4-byte aligned");
+  tattn::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+  a.scale = softmax_scale; a.causal = causal; a.dtype = dtype;
+  return hip_status(tattn::launch_attn_fwd16(a, (hipStream_t)stream), "attn_fwd launch");
+}
+
+int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                 const float* k_scale, const float* v_scale, void* o, float* lse, int B, int N,
+                 int Hq, int Hkv, int d, float softmax_scale, int causal, int out_dtype,
+                 void* stream) {
+  g_last_error[0] = '\0';
+  if (!q8 || !k8 || !v8 || !o || !q_scale || !k_scale || !v_scale)
+    return fail(TATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (int s = check_shape(B, N, Hq, Hkv, d)) return s;
+  if (d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (fp8 path supports 128)", d);
+  if (out_dtype != TATTN_F16 && out_dtype != TATTN_BF16)
+    return fail(TATTN_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(TATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (causal != 0 && causal != 1) return fail(TATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16))
+    return fail(TATTN_ERR_MISALIGNED, "q8, k8, v8, o must be 16-byte aligned");
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4) || (lse && !aligned(lse, 4)))
+    return fail(TATTN_ERR_MISALIGNED, "scales and lse must be 4-byte aligned");
+  tattn::AttnArgs a{};
+  a.q = q8; a.k = k8; a.v = v8; a.o = o; a.lse = lse;
+  a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+  a.scale = softmax_scale; a.causal = causal; a.dtype = out_dtype;
+  return hip_status(tattn::launch_attn_fwd_fp8(a, (hipStream_t)stream), "attn_fwd_fp8 launch");
+}
+
+int hadamard_rotate(const void* x, void* y, const int8_t* signs, float* scales_out, int B, int N,
+                    int H, int d, int in_dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!x || !y) return fail(TATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (int s = check_shape(B, N, H, H, d)) return s;
+  if (d != 64 && d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (in_dtype != TATTN_F16 && in_dtype != TATTN_BF16)
+    return fail(TATTN_ERR_UNSUPPORTED, "in_dtype %d", in_dtype);
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TATTN_ERR_MISALIGNED, "x, y must be 16-byte aligned");
+  if (scales_out && !aligned(scales_out, 4)) return fail(TATTN_ERR_MISALIGNED, "scales_out must be 4-byte aligned");
+  tattn::RotateArgs a{};
+  a.x = x; a.y = y; a.signs = signs; a.scales = scales_out;
+  a.B = B; a.N = N; a.H = H; a.d = d; a.dtype = in_dtype;
+  return hip_status(tattn::launch_hadamard_rotate(a, (hipStream_t)stream), "hadamard_rotate launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, matrix-core
+// wrappers and small utilities.  CDNA4 only (wave64, MFMA).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-bit element traits: storage as raw 16-bit words, 8-element vectors for
+// the 32x32x16 matrix-core instructions.
+struct Bf16 {
+  typedef bf16x8 vec8;
+  __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // round-to-nearest-even fp32 -> bf16 bits
+  __device__ static inline uint16_t from_f32(float x) {
+    __bf16 h = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static inline float to_f32(uint16_t x) {
+    return (float)__builtin_bit_cast(__bf16, x);
+  }
+};
+
+struct F16 {
+  typedef f16x8 vec8;
+  __device__ static inline f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline uint16_t from_f32(float x) {
+    _Float16 h = (_Float16)x;
+    return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static inline float to_f32(uint16_t x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+};
+
+// Pack two fp32 values into one dword of 16-bit codes (low half = a).
+template <typename T>
+__device__ inline uint32_t pack2(float a, float b) {
+  return (uint32_t)T::from_f32(a) | ((uint32_t)T::from_f32(b) << 16);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+}  // namespace tattn
