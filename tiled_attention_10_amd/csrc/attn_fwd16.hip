@@ -1,24 +1,40 @@
 // Fused attention forward, fp16/bf16, for gfx950 (CDNA4).
 //
-// One workgroup = 4 waves = BM = 128 query rows of one (batch, head); each wave
-// owns 32 rows.  The K/V sequence is walked in tiles of BN = 64 keys, staged
-// global -> registers -> LDS in two buffers: tile j+1's loads are issued
-// before tile j is computed and written to the other buffer afterwards, so one
-// barrier per tile covers both the read-after-write and the write-after-read
-// hazard ([FA3-tile] §二's double buffer, with both of its synchronisations).
+// Work decomposition.  One workgroup = 8 waves = BM = 256 query rows of one
+// (batch, head); each wave owns 32 rows and keeps its Q rows in VGPRs for the
+// whole sequence.  The K/V sequence is walked in tiles of BN = 64 keys.  Work
+// items are ordered (batch, head, q tile) and dealt so that consecutive items
+// land on one XCD, which keeps the heads of a KV group (and all q tiles of a
+// head) on one L2.  Causal launches take the longest rows first.
+//
+// Staging ([FA3-tile] §二's double buffer, generalised to three stages).  K and
+// V tiles go global -> LDS directly (16-byte LDS-DMA loads, no VGPR staging)
+// into three-stage rings.  While tile j is consumed, the loads for K(j+3) and
+// V(j+2) are in flight; one barrier per tile both publishes the finished loads
+// (read after write) and retires the stages about to be overwritten (write
+// after read).  LDS rows are unpadded and their 16-byte chunks are XOR-
+// swizzled per row so that the K reads and the transposing V reads are free
+// of bank conflicts.
 //
 // Per tile and wave, on the 32x32x16 matrix cores:
-//   Sᵀ = K·Qᵀ   (A = K rows from LDS, B = the wave's Q rows held in VGPRs for
-//                the whole loop).  The accumulator then holds, in lane l,
-//                32 scores of query row l%32 -- the row statistics are lane-
-//                local apart from one exchange with lane l^32.
-//   online softmax in fp32 ([FA3-V3] §4.2): m' = max(m, rowmax), α = 2^(m−m'),
-//                p = 2^(s·c − m') with c = scale·log2(e), z' = α·z + Σp.
-//   Oᵀ += Vᵀ·Pᵀ (A = Vᵀ from LDS, B = P rounded to the input type).  The
-//                score accumulator's register layout is exactly the B-operand
-//                layout once Vᵀ's key positions are permuted (bits 2 and 3 of
-//                the key index swapped), so P needs no shuffle ([FA3-V3] §7.4's
-//                accumulator-to-operand problem, solved by operand order).
+//   Sᵀ = K·Qᵀ   A = K rows from LDS (rows taken in an order that swaps bits 2
+//                and 3 of the row index), B = Q.  Lane l then holds 32 scores
+//                of query row l%32: row statistics are lane-local apart from
+//                one exchange with lane l^32.
+//   softmax     online, fp32 ([FA3-V3] §4.2): m' = max(m, rowmax), α = 2^(m−m'),
+//                p = 2^(s·c − m') with c = scale·log2(e), z' = α·z + Σp.  The
+//                reference max only moves when a row max grew by more than
+//                kRescaleSlack, which skips the O rescale on almost every tile;
+//                O/z is unchanged in exact arithmetic.
+//   Oᵀ += Vᵀ·Pᵀ A = Vᵀ gathered by transposing LDS reads (ds_read_b64_tr_b16),
+//                B = P rounded to the input type.  Thanks to the K row order
+//                above, the score accumulator already is the B operand, so P
+//                needs no shuffle ([FA3-V3] §7.4's accumulator-to-operand
+//                problem, solved by operand order).
+// The loop is software-pipelined ([FA3-V3] §7.3's intra-warpgroup overlap):
+// tile j+1's score MFMAs are issued in the same basic block as tile j's
+// exponentials and P·V MFMAs, so matrix-core and VALU work of one wave
+// overlap; two waves per SIMD add overlap across waves.
 // The epilogue divides by z (deferred normalisation, [FA3-V3] §11) and writes
 // O and optionally the log-sum-exp.
 #include "tattn_device.hpp"
@@ -28,24 +44,66 @@
 namespace tattn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 128;
-constexpr int BN = 64;
+constexpr int NW = 8;                // waves per workgroup
+constexpr int kThreads = 64 * NW;
+constexpr int BM = 32 * NW;          // query rows per workgroup
+constexpr int BN = 64;               // keys per tile
+constexpr int STAGES = 3;
+
+#ifndef TATTN_RESCALE_SLACK
+#define TATTN_RESCALE_SLACK 8.0f
+#endif
+constexpr float kRescaleSlack = TATTN_RESCALE_SLACK;
 
 template <int D>
-struct Layout {
-  static constexpr int KS = D + 8;    // K row stride in elements (16 B pad)
-  static constexpr int VS = BN + 8;   // Vᵀ row stride in elements (16 B pad)
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int KPT = D / 32;          // keys per thread in the V staging
-  static constexpr int KGROUPS = BN / KPT;    // key groups per tile
-  static constexpr int CHUNKS = D / 8;        // 16-byte chunks per row
+struct Geo {
+  static constexpr int ROWB = 2 * D;                    // bytes per K/V row
+  static constexpr int TILEB = BN * ROWB;               // bytes per tile
+  static constexpr int LDSB = 2 * STAGES * TILEB;       // K ring + V ring
+  static constexpr int LOADS = TILEB / (1024 * NW);     // 1 KB DMA loads per wave per tile
+  static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split into 1 KB loads");
+  // Physical 16-byte chunk = logical chunk ^ swz(row).
+  __device__ static inline int swz(int r) {
+    if constexpr (D == 128) {
+      return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+    } else {
+      const int x = (r >> 1) & 7;
+      return ((x & 3) << 1) | (x >> 2);
+    }
+  }
 };
 
-// Position of key kk (0..63) inside a Vᵀ row: bits 2 and 3 swapped.
-__device__ inline int vt_pos(int kk) { return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1); }
+// Row order of the score MFMA's A operand: bits 2 and 3 swapped.
+__device__ inline int perm23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte LDS-DMA load per lane: lane i's 16 bytes from ``src`` land at LDS
+// byte address ``lds_addr`` + 16·i.  Issued as inline assembly so that the
+// compiler neither treats it as an aliasing LDS store (which would make it wait
+// for the load before every later LDS read) nor counts it: the loop below waits
+// for these loads explicitly with wait_vmcnt before each barrier.  M0 is only
+// written here and consumed by the next instruction.
+__device__ inline void lds_dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "memory");
+}
+
+// Workgroup barrier without a memory fence: the LDS-DMA loads are published by
+// the explicit wait_vmcnt before it; the asm also keeps the compiler from
+// moving LDS accesses across it.
+__device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 struct KernelParams {
   const uint16_t* q;
@@ -58,100 +116,109 @@ struct KernelParams {
 };
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void attn_fwd16_kernel(KernelParams p) {
-  using L = Layout<D>;
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p) {
+  using G = Geo<D>;
   using vec8 = typename T::vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+  typedef __attribute__((address_space(3))) vec8 lds_vec8;
+  constexpr int LOADS = G::LOADS;
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDSB];
+  lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // Work item: consecutive items go to one XCD (workgroups are dealt to the
-  // 8 XCDs round-robin), ordered (batch, head, q tile) so that the heads of a
-  // KV group and all q tiles of a head run close together and share L2.
-  const int G = gridDim.x;
+  const int Gn = gridDim.x;
   const int g = blockIdx.x;
-  const int wi = (G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
+  const int wi = (Gn % 8 == 0) ? (g % 8) * (Gn / 8) + g / 8 : g;
   int qt = wi % p.nqt;
-  if (CAUSAL) qt = p.nqt - 1 - qt;   // longest rows first
+  if (CAUSAL) qt = p.nqt - 1 - qt;
   const int rest = wi / p.nqt;
   const int hq = rest % p.Hq;
   const int b = rest / p.Hq;
   const int hkv = hq / p.group;
   const int N = p.N;
 
-  const long long qs = (long long)p.Hq * D;    // elements between positions
-  const long long kvs = (long long)p.Hkv * D;
+  const long long qs = (long long)p.Hq * D;           // elements between positions
+  const long long kvrow = (long long)p.Hkv * D * 2;   // bytes between key positions
   const uint16_t* qb = p.q + ((long long)b * N * p.Hq + hq) * D;
-  const uint16_t* kb = p.k + ((long long)b * N * p.Hkv + hkv) * D;
-  const uint16_t* vb = p.v + ((long long)b * N * p.Hkv + hkv) * D;
+  const char* kg = (const char*)(p.k + ((long long)b * N * p.Hkv + hkv) * D);
+  const char* vg = (const char*)(p.v + ((long long)b * N * p.Hkv + hkv) * D);
 
   const int q0 = qt * BM;
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + l32;
 
-  // Q fragments (B operand): lane holds Q[qrow][16t + 8hh .. +7].
+  // Q fragments (B operand of the score MFMA): lane holds Q[qrow][16t+8hh .. +7].
   vec8 qf[D / 16];
+  {
+    const uint16_t* qr = qb + (long long)min(qrow, N - 1) * qs + 8 * hh;
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (qrow < N) raw = *(const u32x4*)(qb + qrow * qs + 16 * t + 8 * hh);
-    qf[t] = __builtin_bit_cast(vec8, raw);
+    for (int t = 0; t < D / 16; ++t) qf[t] = __builtin_bit_cast(vec8, *(const u32x4*)(qr + 16 * t));
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int nt = (kv_end + BN - 1) / BN;                    // tiles of the workgroup
+  const int wend = (wq0 >= N) ? 0 : (CAUSAL ? min(kv_end, wq0 + 32) : kv_end);
+  const int ntw = (wend + BN - 1) / BN;                     // tiles this wave computes
 
-  // Staging registers for one K tile and one V tile.
-  u32x4 kst[D / 32], vst[L::KPT];
-  const int vkg = tid % L::KGROUPS, vc = tid / L::KGROUPS;
-
-  auto load_tile = [&](int j) {
-    const int j0 = j * BN;
+  // LDS-DMA geometry: load n of this wave covers tile bytes [1024(wave·LOADS+n), +1024);
+  // lane writes 16 bytes at +16·lane, i.e. row r, physical chunk pc = logical chunk pc^swz(r).
+  int ld_row[LOADS], ld_col[LOADS];
 #pragma unroll
-    for (int r = 0; r < D / 32; ++r) {
-      const int ci = tid + kThreads * r;
-      const int row = ci / L::CHUNKS, c = ci % L::CHUNKS;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (j0 + row < N) raw = *(const u32x4*)(kb + (j0 + row) * kvs + 8 * c);
-      kst[r] = raw;
-    }
+  for (int n = 0; n < LOADS; ++n) {
+    const int o = 1024 * (wave * LOADS + n) + 16 * lane;
+    const int r = o / G::ROWB, pc = (o % G::ROWB) / 16;
+    ld_row[n] = r;
+    ld_col[n] = 16 * (pc ^ G::swz(r));
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  auto issue = [&](const char* gbase, int ring, int stage, int t) {
+    const int j0 = t * BN;
 #pragma unroll
-    for (int e = 0; e < L::KPT; ++e) {
-      const int key = j0 + vkg * L::KPT + e;
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (key < N) raw = *(const u32x4*)(vb + key * kvs + 8 * vc);
-      vst[e] = raw;
+    for (int n = 0; n < LOADS; ++n) {
+      const int row = min(j0 + ld_row[n], N - 1);   // rows past N repeat row N-1 (their p is 0)
+      lds_dma16(gbase + row * kvrow + ld_col[n],
+                lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * L::STAGE;
-    uint16_t* vts = ks + L::K_ELEMS;
+  // Per-lane LDS read offsets within a stage.
+  //  K (score A operand): row kr = perm23(l32) (+32 per key block), chunk 2t+hh.
+  int koff[D / 16];
+  {
+    const int kr = perm23(l32);
 #pragma unroll
-    for (int r = 0; r < D / 32; ++r) {
-      const int ci = tid + kThreads * r;
-      const int row = ci / L::CHUNKS, c = ci % L::CHUNKS;
-      *(u32x4*)(ks + row * L::KS + 8 * c) = kst[r];
-    }
-    // Vᵀ: element x of this thread's 8 channels, for its KPT keys.
-    const int pos = vt_pos(vkg * L::KPT);
+    for (int t = 0; t < D / 16; ++t) koff[t] = kr * G::ROWB + 16 * ((2 * t + hh) ^ G::swz(kr));
+  }
+  //  V (transposing reads): in each 16-lane group, source lane i = 4e + m supplies
+  //  V[key][dv .. dv+3] with key = 16s + 8hh + 4·half + e and dv = 32vq + 16(grp%2) + 4m;
+  //  the group's output lane i then holds V[16s + 8hh + 4·half + 0..3][dv0 + i].
+  int voff[2][D / 32];
+  {
+    const int grp = lane >> 4, i = lane & 15, e = i >> 2, m = i & 3;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      uint32_t w[L::KPT / 2];
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int e2 = 0; e2 < L::KPT / 2; ++e2) {
-        const uint32_t a = vst[2 * e2][x / 2], c = vst[2 * e2 + 1][x / 2];
-        w[e2] = (x & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
+      for (int vq = 0; vq < D / 32; ++vq) {
+        const int key = 8 * hh + 4 * half + e;              // + 16s (swz depends on key % 16 only)
+        const int dv = 32 * vq + 16 * (grp & 1) + 4 * m;
+        voff[half][vq] = key * G::ROWB + 16 * ((dv >> 3) ^ G::swz(key)) + 8 * ((dv >> 2) & 1);
       }
-      uint16_t* dst = vts + (8 * vc + x) * L::VS + pos;
-      if constexpr (L::KPT == 4) {
-        *(u32x2*)dst = u32x2{w[0], w[1]};
-      } else {
-        *(uint32_t*)dst = w[0];
+  }
+
+  auto scores = [&](int stage, f32x16 (&s)[2]) {
+    const lds_char* ks = lds + stage * G::TILEB;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const vec8 a = *(const lds_vec8*)(ks + koff[t] + kq * 32 * G::ROWB);
+        s[kq] = T::mfma(a, qf[t], s[kq]);
       }
-    }
   };
 
   f32x16 oacc[D / 32];
@@ -160,78 +227,97 @@ __global__ __launch_bounds__(kThreads) void attn_fwd16_kernel(KernelParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // Prologue: K0, V0, K1, V1, K2 in flight, then S(0).
+  issue(kg, 0, 0, 0);
+  issue(vg, 1, 0, 0);
+  if (nt > 1) { issue(kg, 0, 1, 1); issue(vg, 1, 1, 1); }
+  if (nt > 2) issue(kg, 0, 2, 2);
+  wait_vmcnt<0>();
+  barrier();
 
-  for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) load_tile(j + 1);
-    const int j0 = j * BN;
-    const uint16_t* ks = smem + (j & 1) * L::STAGE;
-    const uint16_t* vts = ks + L::K_ELEMS;
+  f32x16 scur[2];
+  if (ntw > 0) scores(0, scur);
 
-    if (!(CAUSAL && j0 > wq0 + 31)) {   // wave-uniform: skip fully masked tiles
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          const vec8 a = *(const vec8*)(ks + (32 * kq + l32) * L::KS + 16 * t + 8 * hh);
-          sacc[kq] = T::mfma(a, qf[t], sacc[kq]);
-        }
-      }
-      const bool need_mask = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
-      if (need_mask) {
+  int st0 = 0;   // stage of tile j
+  for (int j = 0; j < nt; ++j) {
+    const int st1 = (st0 == STAGES - 1) ? 0 : st0 + 1;   // stage of tile j+1
+    const int st2 = (st1 == STAGES - 1) ? 0 : st1 + 1;   // stage of tile j+2 (held tile j-1)
+    // Needed now: K(j+1), V(j).  Still allowed in flight: K(j+2), V(j+1) from the last
+    // iteration.  The barrier also retires every wave's reads of K(j) and V(j-1), whose
+    // stages are refilled next (at j = 0: the prologue's reads of K(0)).
+    if (j + 2 < nt) wait_vmcnt<2 * LOADS>();
+    else if (j + 1 < nt) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    barrier();
+    if (j + 3 < nt) issue(kg, 0, st0, j + 3);   // K(j) was consumed in iteration j-1
+    if (j + 2 < nt) issue(vg, 1, st2, j + 2);   // V(j-1) was consumed in iteration j-1
+
+    if (j < ntw) {
+      const int j0 = j * BN;
+      if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0)) {
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = j0 + 32 * kq + 8 * (i / 4) + 4 * hh + (i % 4);
-            if (key >= N || (CAUSAL && key > qrow)) sacc[kq][i] = -INFINITY;
+            const int key = j0 + 32 * kq + 16 * (i >> 3) + 8 * hh + (i & 7);
+            if (key >= N || (CAUSAL && key > qrow)) scur[kq][i] = -INFINITY;
           }
       }
-      float mt = sacc[0][0];
+      float mt = scur[0][0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sacc[0][i]);
+      for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[1][i]);
-      mt = fmaxf(mt, xor32(mt));
-      const float m_new = fmaxf(m_run, mt * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
+      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
+      mt = __builtin_fmaxf(mt, xor32(mt));
+      const float m_cand = mt * c;
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack) != 0) {
+        const float m_new = __builtin_fmaxf(m_run, m_cand);
+        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int vq = 0; vq < D / 32; ++vq)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
+      }
+      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+
+      // Tile j+1's scores (its K stage is ready); overlaps the exponentials below.
+      f32x16 snext[2];
+      scores(st1, snext);
+
+      float pe[32];
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = fast_exp2(fmaf(sacc[kq][i], c, -m_use));
-          sacc[kq][i] = pv;
-          psum += pv;
-        }
-      l_run = l_run * alpha + psum;
+        for (int i = 0; i < 16; ++i) pe[16 * kq + i] = fast_exp2(fmaf(scur[kq][i], c, neg_m));
+      float ps[16];
 #pragma unroll
-      for (int vq = 0; vq < D / 32; ++vq)
+      for (int i = 0; i < 16; ++i) ps[i] = pe[2 * i] + pe[2 * i + 1];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
+      for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) ps[i] = ps[i] + ps[i + w];
+      l_run += ps[0];
 
+      const lds_char* vs = lds + (STAGES + st0) * G::TILEB;
 #pragma unroll
       for (int s = 0; s < BN / 16; ++s) {
-        u32x4 pw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pw[e] = pack2<T>(sacc[s / 2][8 * (s % 2) + 2 * e], sacc[s / 2][8 * (s % 2) + 2 * e + 1]);
-        const vec8 bfrag = __builtin_bit_cast(vec8, pw);
+        const vec8 bfrag = T::pack8(&pe[8 * s]);
 #pragma unroll
         for (int vq = 0; vq < D / 32; ++vq) {
-          const vec8 a = *(const vec8*)(vts + (32 * vq + l32) * L::VS + 16 * s + 8 * hh);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vs + voff[0][vq] + 16 * s * G::ROWB));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(vs + voff[1][vq] + 16 * s * G::ROWB));
+          const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[vq] = T::mfma(a, bfrag, oacc[vq]);
         }
       }
+      scur[0] = snext[0];
+      scur[1] = snext[1];
     }
-
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
-    __syncthreads();
+    st0 = st1;
   }
 
   const float l_tot = l_run + xor32(l_run);

@@ -14,6 +14,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -33,6 +36,14 @@ struct Bf16 {
   __device__ static inline float to_f32(uint16_t x) {
     return (float)__builtin_bit_cast(__bf16, x);
   }
+  // two fp32 -> one dword of bf16 (low half = a), one packed RNE conversion
+  __device__ static inline uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  }
+  __device__ static inline vec8 pack8(const float* x) {
+    u32x4 w = {pack(x[0], x[1]), pack(x[2], x[3]), pack(x[4], x[5]), pack(x[6], x[7])};
+    return __builtin_bit_cast(vec8, w);
+  }
 };
 
 struct F16 {
@@ -47,12 +58,19 @@ struct F16 {
   __device__ static inline float to_f32(uint16_t x) {
     return (float)__builtin_bit_cast(_Float16, x);
   }
+  __device__ static inline uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  }
+  __device__ static inline vec8 pack8(const float* x) {
+    u32x4 w = {pack(x[0], x[1]), pack(x[2], x[3]), pack(x[4], x[5]), pack(x[6], x[7])};
+    return __builtin_bit_cast(vec8, w);
+  }
 };
 
 // Pack two fp32 values into one dword of 16-bit codes (low half = a).
 template <typename T>
 __device__ inline uint32_t pack2(float a, float b) {
-  return (uint32_t)T::from_f32(a) | ((uint32_t)T::from_f32(b) << 16);
+  return T::pack(a, b);
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
