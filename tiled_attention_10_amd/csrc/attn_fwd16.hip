@@ -7,12 +7,12 @@
 // land on one XCD, which keeps the heads of a KV group (and all q tiles of a
 // head) on one L2.  Causal launches take the longest rows first.
 //
-// Staging ([FA3-tile] §二's double buffer, generalised to three stages).  K and
+// Staging ([FA3-tile] §二's double buffer, generalised to four stages).  K and
 // V tiles go global -> LDS directly (16-byte LDS-DMA loads, no VGPR staging)
-// into three-stage rings.  While tile j is consumed, the loads for K(j+3) and
-// V(j+2) are in flight; one barrier per tile both publishes the finished loads
-// (read after write) and retires the stages about to be overwritten (write
-// after read).  LDS rows are unpadded and their 16-byte chunks are XOR-
+// into four-stage rings.  While tile j is consumed, the loads for tiles j+2 and
+// j+3 are in flight; one barrier per tile both publishes the finished loads
+// (read after write) and retires the stage about to be overwritten (write after
+// read).  LDS rows are unpadded and their 16-byte chunks are XOR-
 // swizzled per row so that the K reads and the transposing V reads are free
 // of bank conflicts.
 //
@@ -23,9 +23,10 @@
 //                one exchange with lane l^32.
 //   softmax     online, fp32 ([FA3-V3] §4.2): m' = max(m, rowmax), α = 2^(m−m'),
 //                p = 2^(s·c − m') with c = scale·log2(e), z' = α·z + Σp.  The
-//                reference max only moves when a row max grew by more than
-//                kRescaleSlack, which skips the O rescale on almost every tile;
-//                O/z is unchanged in exact arithmetic.
+//                reference max is set on the first tile and only moves when a
+//                tile's probabilities would leave the 16-bit operand range, which
+//                skips the row max and the O rescale on almost every tile; O/z
+//                is unchanged in exact arithmetic.
 //   Oᵀ += Vᵀ·Pᵀ A = Vᵀ gathered by transposing LDS reads (ds_read_b64_tr_b16),
 //                B = P rounded to the input type.  Thanks to the K row order
 //                above, the score accumulator already is the B operand, so P
@@ -37,6 +38,8 @@
 // overlap; two waves per SIMD add overlap across waves.
 // The epilogue divides by z (deferred normalisation, [FA3-V3] §11) and writes
 // O and optionally the log-sum-exp.
+#include <type_traits>
+
 #include "tattn_device.hpp"
 #include "tattn_launch.hpp"
 #include "tattn.h"
@@ -48,12 +51,11 @@ constexpr int NW = 8;                // waves per workgroup
 constexpr int kThreads = 64 * NW;
 constexpr int BM = 32 * NW;          // query rows per workgroup
 constexpr int BN = 64;               // keys per tile
-constexpr int STAGES = 3;
+constexpr int STAGES = 4;
 
-#ifndef TATTN_RESCALE_SLACK
-#define TATTN_RESCALE_SLACK 8.0f
-#endif
-constexpr float kRescaleSlack = TATTN_RESCALE_SLACK;
+// Largest partial row sum of probabilities accepted before the reference max
+// is moved: keeps every probability below the fp16 operand range.
+constexpr float kOperandLimit = 32768.0f;
 
 template <int D>
 struct Geo {
@@ -174,13 +176,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     ld_col[n] = 16 * (pc ^ G::swz(r));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-  auto issue = [&](const char* gbase, int ring, int stage, int t) {
+  const char* ksrc[LOADS];
+  const char* vsrc[LOADS];
+#pragma unroll
+  for (int n = 0; n < LOADS; ++n) {
+    ksrc[n] = kg + ld_row[n] * kvrow + ld_col[n];
+    vsrc[n] = vg + ld_row[n] * kvrow + ld_col[n];
+  }
+  // Tile t of K (ring 0) or V (ring 1) into ring stage ``stage``.  Whole tiles
+  // advance each lane's pointer by t·BN rows; in a partial last tile, rows past N
+  // repeat row N-1 (their probabilities are 0).
+  auto issue = [&](int ring, int stage, int t) {
     const int j0 = t * BN;
+    const long long adv = (long long)j0 * kvrow;
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
-      const int row = min(j0 + ld_row[n], N - 1);   // rows past N repeat row N-1 (their p is 0)
-      lds_dma16(gbase + row * kvrow + ld_col[n],
-                lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
+      const char* src;
+      if (j0 + BN <= N) {
+        src = (ring ? vsrc[n] : ksrc[n]) + adv;
+      } else {
+        const int row = min(j0 + ld_row[n], N - 1);
+        src = (ring ? vg : kg) + row * kvrow + ld_col[n];
+      }
+      lds_dma16(src, lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
     }
   };
 
@@ -204,11 +222,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       for (int vq = 0; vq < D / 32; ++vq) {
         const int key = 8 * hh + 4 * half + e;              // + 16s (swz depends on key % 16 only)
         const int dv = 32 * vq + 16 * (grp & 1) + 4 * m;
-        voff[half][vq] = key * G::ROWB + 16 * ((dv >> 3) ^ G::swz(key)) + 8 * ((dv >> 2) & 1);
+        voff[half][vq] = STAGES * G::TILEB + key * G::ROWB + 16 * ((dv >> 3) ^ G::swz(key)) +
+                         8 * ((dv >> 2) & 1);
       }
   }
 
-  auto scores = [&](int stage, f32x16 (&s)[2]) {
+  auto scores = [&](const int stage, f32x16 (&s)[2]) {
     const lds_char* ks = lds + stage * G::TILEB;
     s[0] = f32x16{};
     s[1] = f32x16{};
@@ -219,6 +238,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
         const vec8 a = *(const lds_vec8*)(ks + koff[t] + kq * 32 * G::ROWB);
         s[kq] = T::mfma(a, qf[t], s[kq]);
       }
+    // Keep the K reads two MFMAs ahead of their use.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+    for (int i = 0; i < D / 8 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
   };
 
   f32x16 oacc[D / 32];
@@ -226,33 +253,81 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
+  // The two wave groups sharing each SIMD run the phases of a tile in rotated
+  // order ([FA3-V3] §7.3's ping-pong between warpgroups):
+  //   group 0: softmax(j) -> P·V(j) -> scores(j+1)      (scores(0) in the prologue)
+  //   group 1: scores(j)  -> softmax(j) -> P·V(j)
+  // so after each barrier one wave's exponentials meet the other's matrix-core
+  // work.  Both groups read V(j) in step j; group 0 reads K(j+1), group 1 K(j).
+  const bool lead = wave < NW / 2;
 
-  // Prologue: K0, V0, K1, V1, K2 in flight, then S(0).
-  issue(kg, 0, 0, 0);
-  issue(vg, 1, 0, 0);
-  if (nt > 1) { issue(kg, 0, 1, 1); issue(vg, 1, 1, 1); }
-  if (nt > 2) issue(kg, 0, 2, 2);
+  // Prologue: tiles 0..2 of K and V, then scores(0) for group 0.
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < nt) { issue(0, t, t); issue(1, t, t); }
   wait_vmcnt<0>();
   barrier();
 
   f32x16 scur[2];
-  if (ntw > 0) scores(0, scur);
+  if (lead && ntw > 0) scores(0, scur);
 
-  int st0 = 0;   // stage of tile j
-  for (int j = 0; j < nt; ++j) {
-    const int st1 = (st0 == STAGES - 1) ? 0 : st0 + 1;   // stage of tile j+1
-    const int st2 = (st1 == STAGES - 1) ? 0 : st1 + 1;   // stage of tile j+2 (held tile j-1)
-    // Needed now: K(j+1), V(j).  Still allowed in flight: K(j+2), V(j+1) from the last
-    // iteration.  The barrier also retires every wave's reads of K(j) and V(j-1), whose
-    // stages are refilled next (at j = 0: the prologue's reads of K(0)).
+  // One tile; ST = j % STAGES, so every LDS offset is a constant.
+  auto step = [&](auto stc, auto leadc, int j) {
+    constexpr int st = decltype(stc)::value;
+    constexpr bool lead = decltype(leadc)::value;
+    constexpr int stn = (st + 1) % STAGES;
+    // Needed now: K(j+1), V(j).  Allowed in flight: K(j+2), V(j+2) from the last step.
+    // The barrier also retires every wave's reads of K(j-1) and V(j-1), whose stage
+    // receives tile j+3 next.
     if (j + 2 < nt) wait_vmcnt<2 * LOADS>();
-    else if (j + 1 < nt) wait_vmcnt<LOADS>();
     else wait_vmcnt<0>();
     barrier();
-    if (j + 3 < nt) issue(kg, 0, st0, j + 3);   // K(j) was consumed in iteration j-1
-    if (j + 2 < nt) issue(vg, 1, st2, j + 2);   // V(j-1) was consumed in iteration j-1
+    if (j + 3 < nt) {
+      issue(0, (st + 3) % STAGES, j + 3);
+      issue(1, (st + 3) % STAGES, j + 3);
+    }
+    if (j >= ntw) return;
 
-    if (j < ntw) {
+    vec8 pf[BN / 16];
+    // Online softmax of tile j ([FA3-V3] §4.2), fp32 statistics.  The row max is
+    // only taken on the first tile and when the probabilities of a tile would no
+    // longer fit the 16-bit operand range (partial row sum above 2^15, i.e. some
+    // score grew more than 15 in log2 units past the reference max).  Between
+    // those events the reference max stays put; O/z is the same in exact
+    // arithmetic.  The denominator sums the rounded probabilities that enter P·V.
+    auto exps = [&](float neg_m) {
+      float pe[32];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pe[16 * kq + i] = fast_exp2(fmaf(scur[kq][i], c, neg_m));
+#pragma unroll
+      for (int s = 0; s < BN / 16; ++s) pf[s] = T::pack8(&pe[8 * s]);
+      float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+      for (int s = 0; s < BN / 16; s += 2) {
+        ps0 = T::sum8(pf[s], ps0);
+        ps1 = T::sum8(pf[s + 1], ps1);
+      }
+      return ps0 + ps1;
+    };
+    auto rebase = [&]() {
+      float mt = scur[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
+      mt = __builtin_fmaxf(mt, xor32(mt));
+      const float m_new = __builtin_fmaxf(m_run, mt * c);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int vq = 0; vq < D / 32; ++vq)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
+    };
+    auto softmax = [&]() {
       const int j0 = j * BN;
       if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0)) {
 #pragma unroll
@@ -263,47 +338,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
             if (key >= N || (CAUSAL && key > qrow)) scur[kq][i] = -INFINITY;
           }
       }
-      float mt = scur[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
-      mt = __builtin_fmaxf(mt, xor32(mt));
-      const float m_cand = mt * c;
-      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kRescaleSlack) != 0) {
-        const float m_new = __builtin_fmaxf(m_run, m_cand);
-        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int vq = 0; vq < D / 32; ++vq)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
+      if (j == 0) rebase();
+      float psum = exps((m_run == -INFINITY) ? 0.f : -m_run);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= kOperandLimit)) != 0) {
+        rebase();
+        psum = exps((m_run == -INFINITY) ? 0.f : -m_run);
       }
-      const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-
-      // Tile j+1's scores (its K stage is ready); overlaps the exponentials below.
-      f32x16 snext[2];
-      scores(st1, snext);
-
-      float pe[32];
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) pe[16 * kq + i] = fast_exp2(fmaf(scur[kq][i], c, neg_m));
-      float ps[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ps[i] = pe[2 * i] + pe[2 * i + 1];
-#pragma unroll
-      for (int w = 8; w >= 1; w /= 2)
-#pragma unroll
-        for (int i = 0; i < w; ++i) ps[i] = ps[i] + ps[i + w];
-      l_run += ps[0];
-
-      const lds_char* vs = lds + (STAGES + st0) * G::TILEB;
+      l_run += psum;
+    };
+    auto pv = [&]() {
+      const lds_char* vs = lds + st * G::TILEB;   // voff carries the V ring base
 #pragma unroll
       for (int s = 0; s < BN / 16; ++s) {
-        const vec8 bfrag = T::pack8(&pe[8 * s]);
 #pragma unroll
         for (int vq = 0; vq < D / 32; ++vq) {
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -311,14 +357,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_i16x4*)(vs + voff[1][vq] + 16 * s * G::ROWB));
           const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[vq] = T::mfma(a, bfrag, oacc[vq]);
+          oacc[vq] = T::mfma(a, pf[s], oacc[vq]);
         }
       }
-      scur[0] = snext[0];
-      scur[1] = snext[1];
+      // Keep the transposing reads one MFMA ahead of their use.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < BN / 16 * (D / 32) - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    };
+    if constexpr (lead) {
+      softmax();
+      __builtin_amdgcn_sched_barrier(0);
+      pv();
+      __builtin_amdgcn_sched_barrier(0);
+      scores(stn, scur);
+    } else {
+      scores(st, scur);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax();
+      __builtin_amdgcn_sched_barrier(0);
+      pv();
     }
-    st0 = st1;
-  }
+  };
+  // Separate loops per group keep the two schedules' register lifetimes apart.
+  auto run = [&](auto leadc) {
+    for (int j = 0; j < nt; j += STAGES) {
+      step(std::integral_constant<int, 0>{}, leadc, j);
+      if (j + 1 < nt) step(std::integral_constant<int, 1>{}, leadc, j + 1);
+      if (j + 2 < nt) step(std::integral_constant<int, 2>{}, leadc, j + 2);
+      if (j + 3 < nt) step(std::integral_constant<int, 3>{}, leadc, j + 3);
+    }
+  };
+  if (lead) run(std::true_type{});
+  else run(std::false_type{});
 
   const float l_tot = l_run + xor32(l_run);
   if (qrow < N) {

@@ -44,6 +44,17 @@ struct Bf16 {
     u32x4 w = {pack(x[0], x[1]), pack(x[2], x[3]), pack(x[4], x[5]), pack(x[6], x[7])};
     return __builtin_bit_cast(vec8, w);
   }
+  // acc + sum of the 8 elements (four 2-element dot products with ones, fp32 accumulate)
+  // (Pairs are taken with shufflevector: bit-casting single elements of a 4-dword
+  // vector to bf16x2 was miscompiled into four uses of element 0.)
+  __device__ static inline float sum8(vec8 v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+    return acc;
+  }
 };
 
 struct F16 {
@@ -64,6 +75,14 @@ struct F16 {
   __device__ static inline vec8 pack8(const float* x) {
     u32x4 w = {pack(x[0], x[1]), pack(x[2], x[3]), pack(x[4], x[5]), pack(x[6], x[7])};
     return __builtin_bit_cast(vec8, w);
+  }
+  __device__ static inline float sum8(vec8 v, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+    return acc;
   }
 };
 
