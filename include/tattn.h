@@ -89,7 +89,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   q_scale, k_scale, v_scale  fp32 [B, Hq|Hkv, ceil(N/64)], finite and > 0
  *   o                       [B, N, Hq, d] in out_dtype (TATTN_BF16 or TATTN_F16)
  *   lse                     as for attn_fwd, or NULL
- *   other arguments as for attn_fwd (d = 128 only on this path).
+ *   other arguments as for attn_fwd (d = 128 and N <= 262144 on this path:
+ *   larger values return TATTN_ERR_UNSUPPORTED).
  */
 int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                  const float* q_scale, const float* k_scale, const float* v_scale,

@@ -94,6 +94,7 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const 
     return fail(TATTN_ERR_INVALID_ARG, "null tensor pointer");
   if (int s = check_shape(B, N, Hq, Hkv, d)) return s;
   if (d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (fp8 path supports 128)", d);
+  if (N > 262144) return fail(TATTN_ERR_UNSUPPORTED, "N = %d > 262144 on the fp8 path", N);
   if (out_dtype != TATTN_F16 && out_dtype != TATTN_BF16)
     return fail(TATTN_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
