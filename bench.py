@@ -1,21 +1,29 @@
 """Benchmark of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--causal 0|1]
-                    [--dtype bf16|fp16|fp8] [--no-cpu-baseline]
+                    [--dtype bf16|fp16|fp8] [--no-cpu-baseline] [--no-fp8] [--copy-calibration]
 
-A step is one attention forward over the workload's synthetic Q, K, V (already
-resident in HBM).  The default workload is one layer of a 70B-class model
-with grouped KV heads (B=1, 64 query heads over 8 KV heads, N=8192, d=128),
-run non-causal in bf16.  Prints ONE JSON line with the throughput in TFLOPS
-(4·N²·d·Hq·B per step, halved when causal), the roofline of the attention
-kernel against the dense bf16 matrix-core peak, and the CPU oracle timed on a
-bounded row sample of the same workload.
+A step is one attention forward over the workload's synthetic Q, K, V, already
+resident in HBM.  The default workload is one layer of a 70B-class model with
+grouped KV heads (B=1, 64 query heads over 8 KV heads, N=8192, d=128), run
+non-causal in bf16 (the "bf16, non-causal, d=128, N >= 8k" operating point).
+With --dtype fp8 a step is attn_fwd_fp8 on E4M3 codes prepared once by
+hadamard_rotate (rotation + quantisation, timed separately as the prologue).
+
+Prints ONE JSON line: throughput in TFLOPS (4·N²·d·Hq·B per step, halved when
+causal), the attention kernel's roofline against the dense matrix-core peak,
+its HBM traffic when a counter measurement of the current kernel source is on
+record under profiles/, the fp8 leg on the same shape (unless --no-fp8 or
+--dtype fp8), and the CPU oracle timed on a bounded row sample of the workload.
+
+--copy-calibration runs only a plain device copy of known size (for scaling
+the FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exits.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -23,7 +31,11 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2}   # dense matrix-core peaks
+# Dense matrix-core peaks of MI355X (TFLOP/s)
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2}
+KERNEL_SOURCES = {"attn_fwd16_kernel": ["attn_fwd16.hip", "tattn_pipeline.hpp", "tattn_device.hpp"],
+                  "attn_fwd_fp8_kernel": ["attn_fwd_fp8.hip", "tattn_pipeline.hpp", "tattn_device.hpp"]}
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -33,10 +45,31 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_bf16_h64kv8_n8192")
     ap.add_argument("--causal", type=int, default=0)
-    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="query rows per head in the oracle sample")
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows per head in the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "tiled_attention_10_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from a counter run of this exact kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}:{workload}")
+    if not rec or rec.get("source_sha") != source_hash(kernel):
+        return None
+    return rec.get("traffic_bytes")
 
 
 def cpu_baseline(q, k, v, causal, rows_per_head, seed):
@@ -59,9 +92,37 @@ def cpu_baseline(q, k, v, causal, rows_per_head, seed):
         flops = sum(4.0 * (int(r) + 1) * d for r in rows) * Hq * B
     else:
         flops = 4.0 * len(rows) * N * d * Hq * B
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(rows)} random query rows x {Hq} heads x B={B} (exact fp64 rows), "
                       f"{flops:.3e} flop in {dt:.2f} s"}
+
+
+def time_launches(torch, fn, steps, warmup, stream):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+
+def fp8_inputs(T, torch, W, w, q, k, v, dev):
+    signs = torch.from_numpy(W.rotation_signs(w.wid, w.d)).to(dev)
+    q8, sq = T.hadamard_rotate(q, signs, quantize=True)
+    k8, sk = T.hadamard_rotate(k, signs, quantize=True)
+    v8, sv = T.hadamard_rotate(v, None, quantize=True)
+
+    def prologue():
+        T.hadamard_rotate(q, signs, quantize=True, out=q8, scales=sq)
+        T.hadamard_rotate(k, signs, quantize=True, out=k8, scales=sk)
+        T.hadamard_rotate(v, None, quantize=True, out=v8, scales=sv)
+
+    return (q8, k8, v8, sq, sk, sv), prologue
 
 
 def main():
@@ -74,29 +135,42 @@ def main():
     import tiled_attention_10_amd as T
     from tiled_attention_10_amd import workloads as W
 
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return
+
     w = W.WORKLOADS[args.workload]
     causal = bool(args.causal)
-    dev = torch.device("cuda:0")
-    q, k, v = (W.to_torch(x, args.dtype) for x in W.qkv_f32(w))
+    src_dtype = "bf16" if args.dtype == "fp8" else args.dtype
+    q, k, v = (W.to_torch(x, src_dtype) for x in W.qkv_f32(w))
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    out = torch.empty_like(qd)
+    out = torch.empty(qd.shape, dtype=torch.bfloat16 if args.dtype == "fp8" else qd.dtype, device=dev)
     print(f"[bench] {w.name} dtype={args.dtype} causal={causal} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
-
-    for _ in range(args.warmup):
-        T.attn_fwd(qd, kd, vd, causal=causal, out=out)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        T.attn_fwd(qd, kd, vd, causal=causal, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
     flops = w.flops(causal)
+    wl_name = w.name + ("_causal" if causal else "_noncausal")
+
+    extra = {}
+    if args.dtype == "fp8":
+        ins, prologue = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
+        kernel = "attn_fwd_fp8_kernel"
+        ms, wall = time_launches(torch, lambda: T.attn_fwd_fp8(*ins, causal=causal, out=out),
+                                 args.steps, args.warmup, stream)
+        pms, _ = time_launches(torch, prologue, max(3, args.steps // 4), 2, stream)
+        extra["prologue_ms"] = round(pms, 4)
+        extra["with_prologue_tflops"] = round(flops / ((ms + pms) * 1e-3) / 1e12, 2)
+    else:
+        kernel = "attn_fwd16_kernel"
+        ms, wall = time_launches(torch, lambda: T.attn_fwd(qd, kd, vd, causal=causal, out=out),
+                                 args.steps, args.warmup, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.dtype]
 
@@ -113,13 +187,24 @@ def main():
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name + ("_causal" if causal else "_noncausal"), "B": w.B, "N": w.N,
-                   "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": causal},
+        "config": {"workload": wl_name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "causal": causal},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None,
-                     "kernel": "attn_fwd16_kernel", "flop_per_launch": flops},
+                     "frac": round(tflops / peak, 4), "traffic": recorded_traffic(kernel, wl_name),
+                     "kernel": kernel, "flop_per_launch": flops, "source_sha": source_hash(kernel)},
         "wall_s_timed": round(wall, 3),
     }
+    res.update(extra)
+    if args.dtype != "fp8" and not args.no_fp8 and w.d == 128:
+        ins, prologue = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
+        out8 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
+        fms, _ = time_launches(torch, lambda: T.attn_fwd_fp8(*ins, causal=causal, out=out8),
+                               max(5, args.steps // 2), 3, stream)
+        pms, _ = time_launches(torch, prologue, 5, 2, stream)
+        res["fp8"] = {"ms_per_step": round(fms, 4), "tflops": round(flops / (fms * 1e-3) / 1e12, 2),
+                      "frac_of_fp8_peak": round(flops / (fms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                      "prologue_ms": round(pms, 4), "speedup_vs_" + args.dtype: round(ms / fms, 3),
+                      "speedup_incl_prologue": round(ms / (fms + pms), 3)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, causal, args.cpu_rows, w.wid)
     print(json.dumps(res), flush=True)

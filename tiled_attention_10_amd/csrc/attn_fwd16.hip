@@ -145,29 +145,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     ld_col[n] = 16 * (pc ^ G::swz(r));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-  const char* ksrc[LOADS];
-  const char* vsrc[LOADS];
+  uint32_t ld_off[LOADS];   // byte offset of this lane's 16 bytes within a tile (same for K and V)
 #pragma unroll
-  for (int n = 0; n < LOADS; ++n) {
-    ksrc[n] = kg + ld_row[n] * kvrow + ld_col[n];
-    vsrc[n] = vg + ld_row[n] * kvrow + ld_col[n];
-  }
-  // Tile t of K (ring 0) or V (ring 1) into ring stage ``stage``.  Whole tiles
-  // advance each lane's pointer by t·BN rows; in a partial last tile, rows past N
-  // repeat row N-1 (their probabilities are 0).
+  for (int n = 0; n < LOADS; ++n) ld_off[n] = (uint32_t)(ld_row[n] * kvrow + ld_col[n]);
+  // Tile t of K (ring 0) or V (ring 1) into ring stage ``stage``.  The tile base
+  // is wave-uniform; in a partial last tile, rows past N repeat row N-1 (their
+  // probabilities are 0).
   auto issue = [&](int ring, int stage, int t) {
     const int j0 = t * BN;
-    const long long adv = (long long)j0 * kvrow;
+    const char* base = (ring ? vg : kg) + (long long)j0 * kvrow;
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
-      const char* src;
-      if (j0 + BN <= N) {
-        src = (ring ? vsrc[n] : ksrc[n]) + adv;
-      } else {
-        const int row = min(j0 + ld_row[n], N - 1);
-        src = (ring ? vg : kg) + row * kvrow + ld_col[n];
-      }
-      lds_dma16(src, lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
+      uint32_t off = ld_off[n];
+      if (j0 + BN > N) off = (uint32_t)((min(j0 + ld_row[n], N - 1) - j0) * kvrow + ld_col[n]);
+      lds_dma16(base, off, lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
     }
   };
 
@@ -365,8 +356,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   else run(std::false_type{});
 
   const float l_tot = l_run + xor32(l_run);
-  if (qrow < N) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // The rings are free once every wave has left the loop; each wave stages its rows in 8 KB.
+  __syncthreads();
+  if constexpr (D == 128) {
+    store_rows<T>(lds + wave * 8192, oacc, inv, lane, p.o + ((long long)b * N * p.Hq + hq) * D + wq0 * qs,
+                  qs, N - wq0);
+  } else if (qrow < N) {
     uint16_t* orow = p.o + ((long long)b * N * p.Hq + hq) * D + qrow * qs;
 #pragma unroll
     for (int vq = 0; vq < D / 32; ++vq)
@@ -377,10 +373,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
         w[1] = pack2<T>(oacc[vq][4 * a + 2] * inv, oacc[vq][4 * a + 3] * inv);
         *(u32x2*)(orow + 32 * vq + 8 * a + 4 * hh) = w;
       }
-    if (p.lse != nullptr && hh == 0)
-      p.lse[((long long)b * p.Hq + hq) * N + qrow] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
+  if (qrow < N && p.lse != nullptr && hh == 0)
+    p.lse[((long long)b * p.Hq + hq) * N + qrow] =
+        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D, bool CAUSAL>

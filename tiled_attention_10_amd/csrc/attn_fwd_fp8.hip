@@ -144,19 +144,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   // LDS-DMA: one 1 KB load per wave per tile = rows 8·wave .. 8·wave+7.
   const int ld_row = 8 * wave + (lane >> 3);
   const int ld_col = 16 * ((lane & 7) ^ swz(ld_row));
-  const char* ksrc = kg + ld_row * kvrow + ld_col;
-  const char* vsrc = vg + ld_row * kvrow + ld_col;
+  const uint32_t ld_off = (uint32_t)(ld_row * kvrow + ld_col);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
   auto issue = [&](int ring, int stage, int t) {
     const int j0 = t * BN;
-    const char* src;
-    if (j0 + BN <= N) {
-      src = (ring ? vsrc : ksrc) + (long long)j0 * kvrow;
-    } else {
-      const int row = min(j0 + ld_row, N - 1);   // rows past N repeat row N-1 (their p is 0)
-      src = (ring ? vg : kg) + row * kvrow + ld_col;
-    }
-    lds_dma16(src, lds_base + (ring * STAGES + stage) * TILEB + 1024 * wave);
+    const char* base = (ring ? vg : kg) + (long long)j0 * kvrow;
+    uint32_t off = ld_off;
+    if (j0 + BN > N) off = (uint32_t)((min(j0 + ld_row, N - 1) - j0) * kvrow + ld_col);   // rows past N repeat row N-1
+    lds_dma16(base, off, lds_base + (ring * STAGES + stage) * TILEB + 1024 * wave);
   };
 
   // K reads: row kr = perm23(l32) (+32 per key block), 16-byte chunks 4t + 2hh + u.
@@ -313,22 +308,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   else run(std::false_type{});
 
   const float l_tot = l_run + xor32(l_run);
-  if (qrow < N) {
-    const float inv = l_tot > 0.f ? vmax * 0.00390625f / l_tot : 0.f;   // max(sv)·2^-8 / z
-    uint16_t* orow = p.o + ((long long)b * N * p.Hq + hq) * D + qrow * qstride;
-#pragma unroll
-    for (int vq = 0; vq < D / 32; ++vq)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2 w;
-        w[0] = pack2<OutT>(oacc[vq][4 * a + 0] * inv, oacc[vq][4 * a + 1] * inv);
-        w[1] = pack2<OutT>(oacc[vq][4 * a + 2] * inv, oacc[vq][4 * a + 3] * inv);
-        *(u32x2*)(orow + 32 * vq + 8 * a + 4 * hh) = w;
-      }
-    if (p.lse != nullptr && hh == 0)
-      p.lse[((long long)b * p.Hq + hq) * N + qrow] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  }
+  const float inv = l_tot > 0.f ? vmax * 0.00390625f / l_tot : 0.f;   // max(sv)·2^-8 / z
+  // The rings are free once every wave has left the loop; each wave stages its rows in 8 KB.
+  __syncthreads();
+  store_rows<OutT>(lds + wave * 8192, oacc, inv, lane, p.o + ((long long)b * N * p.Hq + hq) * D + wq0 * qstride,
+                   qstride, N - wq0);
+  if (qrow < N && p.lse != nullptr && hh == 0)
+    p.lse[((long long)b * p.Hq + hq) * N + qrow] =
+        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <typename OutT, bool CAUSAL>

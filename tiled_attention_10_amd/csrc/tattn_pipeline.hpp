@@ -34,9 +34,51 @@ __device__ inline void lds_dma16(const void* src, uint32_t lds_addr) {
                : "memory");
 }
 
+// Same, with a wave-uniform base pointer and a 32-bit per-lane byte offset.
+__device__ inline void lds_dma16(const void* base, uint32_t offset, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(offset), "s"(base)
+               : "memory");
+}
+
 // Workgroup barrier without a memory fence: the LDS-DMA loads are published by
 // the explicit wait_vmcnt before it; the asm also keeps the compiler from
 // moving LDS accesses across it.
 __device__ inline void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Epilogue store of one wave's 32 x 128 output rows.  The Oᵀ accumulator gives
+// each lane one row and 4-element runs of channels, which would make every store
+// instruction touch 32 rows with 16 bytes each; instead the wave stages its rows
+// in an 8 KB LDS block (16-byte chunk c of row r kept at chunk c ^ (r % 16), so
+// both the 8-byte writes and the 16-byte reads are free of bank conflicts) and
+// writes them back 16 bytes per lane, four whole 256-byte rows per instruction.
+//   oacc[vq][4a + e] = O[row l%32][32vq + 8a + 4(l/32) + e] (already normalised
+//   by ``inv``); ``out`` points at row 0 of the wave, rows ``rowstride`` elements
+//   apart; only rows < ``nvalid`` are written.
+template <typename T, typename F32x16>
+__device__ inline void store_rows(__attribute__((address_space(3))) char* stage, const F32x16 (&oacc)[4],
+                                  float inv, int lane, uint16_t* out, long long rowstride, int nvalid) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int vq = 0; vq < 4; ++vq)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int u = 8 * vq + 2 * a + hh;        // 8-byte unit within the row
+      const int c = u >> 1;
+      u32x2_t w;
+      w[0] = T::pack(oacc[vq][4 * a + 0] * inv, oacc[vq][4 * a + 1] * inv);
+      w[1] = T::pack(oacc[vq][4 * a + 2] * inv, oacc[vq][4 * a + 3] * inv);
+      *(__attribute__((address_space(3))) u32x2_t*)(stage + r * 256 + 16 * (c ^ (r & 15)) + 8 * (u & 1)) = w;
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = 64 * i + lane, row = idx >> 4, c = idx & 15;
+    const u32x4_t v = *(__attribute__((address_space(3))) u32x4_t*)(stage + row * 256 + 16 * (c ^ (row & 15)));
+    if (row < nvalid) *(u32x4_t*)(out + row * rowstride + 8 * c) = v;
+  }
+}
 
 }  // namespace tattn
