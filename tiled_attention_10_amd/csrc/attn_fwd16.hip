@@ -65,16 +65,44 @@ struct Geo {
   static constexpr int LDSB = 2 * STAGES * TILEB;       // K ring + V ring
   static constexpr int LOADS = TILEB / (1024 * NW);     // 1 KB DMA loads per wave per tile
   static_assert(LOADS >= 1 && TILEB % (1024 * NW) == 0, "tile must split into 1 KB loads");
-  // Physical 16-byte chunk = logical chunk ^ swz(row).
+  // Physical 16-byte chunk = logical chunk ^ swz(row).  Conflict-free for both read kinds:
+  // a 16-lane group of K reads (ds_read_b128, 16 distinct rows, one 16-byte chunk each) and
+  // a 32-lane half-wave of V transposing reads (ds_read_b64_tr_b16, 4 consecutive keys x
+  // 4 consecutive logical chunks starting at a multiple of 4) both land on 16 distinct
+  // 16-byte bank windows.  Depends on row % 16 only.
   __device__ static inline int swz(int r) {
     if constexpr (D == 128) {
-      return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+      return ((r & 3) << 2) | ((r >> 2) & 3);
     } else {
-      const int x = (r >> 1) & 7;
-      return ((x & 3) << 1) | (x >> 2);
+      return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
     }
   }
 };
+
+#ifndef TATTN_READ_AHEAD
+#define TATTN_READ_AHEAD 2
+#endif
+// Products between an LDS read and the product that consumes it.
+constexpr int kReadAhead = TATTN_READ_AHEAD;
+
+// Scheduling order of a stream of NPV P·V products (two transposing LDS reads
+// each) and NSC score products (one LDS read each): the reads of the first
+// kReadAhead products, then each product followed by the reads of the product
+// kReadAhead places later.
+template <int NPV, int NSC, int I = 0>
+__device__ inline void mma_stream_order() {
+  constexpr int N = NPV + NSC;
+  constexpr int A = kReadAhead < N ? kReadAhead : N;
+  if constexpr (I == 0) {
+    constexpr int lead_reads = 2 * (A < NPV ? A : NPV) + (A > NPV ? A - NPV : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, lead_reads, 0);
+  }
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + A < N) __builtin_amdgcn_sched_group_barrier(0x100, (I + A < NPV) ? 2 : 1, 0);
+    mma_stream_order<NPV, NSC, I + 1>();
+  }
+}
 
 struct KernelParams {
   const uint16_t* q;
@@ -148,18 +176,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   uint32_t ld_off[LOADS];   // byte offset of this lane's 16 bytes within a tile (same for K and V)
 #pragma unroll
   for (int n = 0; n < LOADS; ++n) ld_off[n] = (uint32_t)(ld_row[n] * kvrow + ld_col[n]);
-  // Tile t of K (ring 0) or V (ring 1) into ring stage ``stage``.  The tile base
-  // is wave-uniform; in a partial last tile, rows past N repeat row N-1 (their
-  // probabilities are 0).
-  auto issue = [&](int ring, int stage, int t) {
-    const int j0 = t * BN;
-    const char* base = (ring ? vg : kg) + (long long)j0 * kvrow;
+  // Offsets for the last tile: rows past N repeat row N-1 (their probabilities are 0).
+  uint32_t ld_off_last[LOADS];
+  {
+    const int jl = (nt - 1) * BN;
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      uint32_t off = ld_off[n];
-      if (j0 + BN > N) off = (uint32_t)((min(j0 + ld_row[n], N - 1) - j0) * kvrow + ld_col[n]);
-      lds_dma16(base, off, lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
-    }
+    for (int n = 0; n < LOADS; ++n)
+      ld_off_last[n] = (uint32_t)((min(jl + ld_row[n], N - 1) - jl) * kvrow + ld_col[n]);
+  }
+  // Tile t of K (ring 0) or V (ring 1) into ring stage ``stage``.  Tiles past the
+  // end repeat the last tile (into a stage nobody reads again), so every wave issues
+  // the same loads in every step and every address stays inside K and V.
+  auto issue = [&](int ring, int stage, int t) {
+    t = min(t, nt - 1);
+    const char* base = (ring ? vg : kg) + (long long)(t * BN) * kvrow;
+    const bool last = t == nt - 1;
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n)
+      lds_dma16(base, last ? ld_off_last[n] : ld_off[n],
+                lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
   };
 
   // Per-lane LDS read offsets within a stage.
@@ -187,6 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       }
   }
 
+  // Score product S^T = K·Q^T of one K stage into s[2] (keys 0..31 and 32..63).
   auto scores = [&](const int stage, f32x16 (&s)[2]) {
     const lds_char* ks = lds + stage * G::TILEB;
     s[0] = f32x16{};
@@ -198,57 +234,78 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
         const vec8 a = *(const lds_vec8*)(ks + koff[t] + kq * 32 * G::ROWB);
         s[kq] = T::mfma(a, qf[t], s[kq]);
       }
-    // Keep the K reads two MFMAs ahead of their use.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-#pragma unroll
-    for (int i = 0; i < D / 8 - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
   };
 
+  f32x16 scur[2];   // scores of the tile whose softmax comes next
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
-  // The two wave groups sharing each SIMD run the phases of a tile in rotated
-  // order ([FA3-V3] §7.3's ping-pong between warpgroups):
-  //   group 0: softmax(j) -> P·V(j) -> scores(j+1)      (scores(0) in the prologue)
-  //   group 1: scores(j)  -> softmax(j) -> P·V(j)
-  // so after each barrier one wave's exponentials meet the other's matrix-core
-  // work.  Both groups read V(j) in step j; group 0 reads K(j+1), group 1 K(j).
+  // The two wave groups sharing each SIMD alternate between exponentials and
+  // matrix-core work ([FA3-V3] §7.3's ping-pong between warpgroups).  In step j:
+  //   group 0: softmax(j)              | P·V(j), scores(j+1)   (scores(0) in the prologue)
+  //   group 1: P·V(j-1), scores(j)     | softmax(j)            (P·V(last) after the loop)
+  // so each wave's softmax runs while the other wave of its SIMD issues both of
+  // its products.  Step j reads K(j), K(j+1), V(j-1) and V(j).
   const bool lead = wave < NW / 2;
+  vec8 pf[BN / 16];   // probabilities of the last softmax (operand of the next P·V)
 
-  // Prologue: tiles 0..2 of K and V, then scores(0) for group 0.
+  // Prologue: K tiles 0..2 and V tiles 0..1, then scores(0) for group 0.
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < nt) { issue(0, t, t); issue(1, t, t); }
+  for (int t = 0; t < STAGES - 1; ++t) {
+    if (t < nt) issue(0, t, t);
+    if (t < STAGES - 2 && t < nt) issue(1, t, t);
+  }
   wait_vmcnt<0>();
   barrier();
 
-  f32x16 scur[2];
-  if (lead && ntw > 0) scores(0, scur);
+  // O^T += V^T·P^T for one V stage, with the probabilities in pf.
+  auto pv = [&](const int vst) {
+    const lds_char* vs = lds + vst * G::TILEB;   // voff carries the V ring base
+#pragma unroll
+    for (int s = 0; s < BN / 16; ++s) {
+#pragma unroll
+      for (int vq = 0; vq < D / 32; ++vq) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs + voff[0][vq] + 16 * s * G::ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs + voff[1][vq] + 16 * s * G::ROWB));
+        const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[vq] = T::mfma(a, pf[s], oacc[vq]);
+      }
+    }
+  };
+  // Each matrix-core phase issues every LDS read kReadAhead products before the
+  // product that consumes it.
+  auto pv_only = [&](const int vst) {
+    pv(vst);
+    mma_stream_order<BN / 16 * (D / 32), 0>();
+  };
+  auto scores_only = [&](const int kst) {
+    scores(kst, scur);
+    mma_stream_order<0, D / 8>();
+  };
+
+  if (lead && ntw > 0) scores_only(0);
 
   // One tile; ST = j % STAGES, so every LDS offset is a constant.
   auto step = [&](auto stc, auto leadc, int j) {
     constexpr int st = decltype(stc)::value;
     constexpr bool lead = decltype(leadc)::value;
     constexpr int stn = (st + 1) % STAGES;
-    // Needed now: K(j+1), V(j).  Allowed in flight: K(j+2), V(j+2) from the last step.
-    // The barrier also retires every wave's reads of K(j-1) and V(j-1), whose stage
-    // receives tile j+3 next.
-    if (j + 2 < nt) wait_vmcnt<2 * LOADS>();
-    else wait_vmcnt<0>();
+    constexpr int stp = (st + STAGES - 1) % STAGES;
+    // Needed now: K(j+1) and V(j), issued two steps ago.  Allowed in flight: K(j+2)
+    // and V(j+1) from the last step.  The barrier also retires every wave's reads
+    // of K(j-1) and V(j-2), whose stages receive K(j+3) and V(j+2) in this step.
+    wait_vmcnt<2 * LOADS>();
     barrier();
-    if (j + 3 < nt) {
-      issue(0, (st + 3) % STAGES, j + 3);
-      issue(1, (st + 3) % STAGES, j + 3);
-    }
-    if (j >= ntw) return;
+    // The tile loads of a step go out at two points of each wave's schedule, which
+    // differ between the groups: issued all at once, the loads of eight waves queue
+    // in the address unit and stall the issuing waves.
+    auto load_k = [&]() { issue(0, (st + 3) % STAGES, j + 3); };
+    auto load_v = [&]() { issue(1, (st + 2) % STAGES, j + 2); };
 
-    vec8 pf[BN / 16];
     // Online softmax of tile j ([FA3-V3] §4.2), fp32 statistics.  The row max is
     // only taken on the first tile and when the probabilities of a tile would no
     // longer fit the 16-bit operand range (partial row sum above 2^15, i.e. some
@@ -306,41 +363,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       }
       l_run += psum;
     };
-    auto pv = [&]() {
-      const lds_char* vs = lds + st * G::TILEB;   // voff carries the V ring base
-#pragma unroll
-      for (int s = 0; s < BN / 16; ++s) {
-#pragma unroll
-        for (int vq = 0; vq < D / 32; ++vq) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vs + voff[0][vq] + 16 * s * G::ROWB));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(vs + voff[1][vq] + 16 * s * G::ROWB));
-          const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[vq] = T::mfma(a, pf[s], oacc[vq]);
-        }
-      }
-      // Keep the transposing reads one MFMA ahead of their use.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < BN / 16 * (D / 32) - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    };
     if constexpr (lead) {
+      if (j >= ntw) {
+        load_k();
+        load_v();
+        return;
+      }
       softmax();
       __builtin_amdgcn_sched_barrier(0);
-      pv();
-      __builtin_amdgcn_sched_barrier(0);
-      scores(stn, scur);
+      load_k();
+      pv_only(st);
+      load_v();
+      if (j + 1 < ntw) scores_only(stn);
     } else {
-      scores(st, scur);
+      const bool has_pv = j >= 1 && j - 1 < ntw, has_scores = j < ntw;
+      load_k();
+      if (has_pv) pv_only(stp);
+      load_v();
+      if (has_scores) scores_only(st);
+      if (!has_scores) return;
       __builtin_amdgcn_sched_barrier(0);
       softmax();
-      __builtin_amdgcn_sched_barrier(0);
-      pv();
     }
   };
   // Separate loops per group keep the two schedules' register lifetimes apart.
@@ -352,8 +395,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       if (j + 3 < nt) step(std::integral_constant<int, 3>{}, leadc, j + 3);
     }
   };
-  if (lead) run(std::true_type{});
-  else run(std::false_type{});
+  if (lead) {
+    run(std::true_type{});
+  } else {
+    run(std::false_type{});
+    if (ntw == nt && nt > 0) pv_only((nt - 1) % STAGES);
+  }
+  wait_vmcnt<0>();   // the last steps' loads land in the rings reused below
 
   const float l_tot = l_run + xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
