@@ -149,12 +149,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + l32;
 
-  // Q fragments (B operand of the score MFMA): lane holds Q[qrow][16t+8hh .. +7].
+  // Q fragments (B operand of the score MFMA): lane holds c·Q[qrow][16t+8hh .. +7],
+  // c = scale·log2(e), rounded to the input type, so that scores come out in log2 units.
   vec8 qf[D / 16];
   {
     const uint16_t* qr = qb + (long long)min(qrow, N - 1) * qs + 8 * hh;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) qf[t] = __builtin_bit_cast(vec8, *(const u32x4*)(qr + 16 * t));
+    for (int t = 0; t < D / 16; ++t) {
+      const vec8 raw = __builtin_bit_cast(vec8, *(const u32x4*)(qr + 16 * t));
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (float)raw[e] * p.c;
+      qf[t] = T::pack8(x);
+    }
   }
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
@@ -222,11 +229,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       }
   }
 
+  f32x16 scur[2];   // scores of the tile whose softmax comes next, minus m_ref
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+  // Reference max of the row (log2 units) and its negation in every element of an
+  // accumulator: the score products start from it, so a score arrives as s - m_ref.
+  float m_ref = 0.f, l_run = 0.f;
+  f32x16 negm = {};
+
   // Score product S^T = K·Q^T of one K stage into s[2] (keys 0..31 and 32..63).
   auto scores = [&](const int stage, f32x16 (&s)[2]) {
     const lds_char* ks = lds + stage * G::TILEB;
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+    s[0] = negm;
+    s[1] = negm;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
 #pragma unroll
@@ -236,12 +252,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       }
   };
 
-  f32x16 scur[2];   // scores of the tile whose softmax comes next
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c = p.c;
   // The two wave groups sharing each SIMD alternate between exponentials and
   // matrix-core work ([FA3-V3] §7.3's ping-pong between warpgroups).  In step j:
   //   group 0: softmax(j)              | P·V(j), scores(j+1)   (scores(0) in the prologue)
@@ -312,12 +322,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     // score grew more than 15 in log2 units past the reference max).  Between
     // those events the reference max stays put; O/z is the same in exact
     // arithmetic.  The denominator sums the rounded probabilities that enter P·V.
-    auto exps = [&](float neg_m) {
+    // ``shift`` is zero except right after the reference max moved.
+    auto exps = [&](auto shifted, float shift) {
       float pe[32];
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pe[16 * kq + i] = fast_exp2(fmaf(scur[kq][i], c, neg_m));
+        for (int i = 0; i < 16; ++i) {
+          if constexpr (decltype(shifted)::value) pe[16 * kq + i] = fast_exp2(scur[kq][i] - shift);
+          else pe[16 * kq + i] = fast_exp2(scur[kq][i]);
+        }
 #pragma unroll
       for (int s = 0; s < BN / 16; ++s) pf[s] = T::pack8(&pe[8 * s]);
       float ps0 = 0.f, ps1 = 0.f;
@@ -328,21 +342,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       }
       return ps0 + ps1;
     };
-    auto rebase = [&]() {
+    // Moves the reference max to the row max of this tile and returns the shift.
+    // On the first tile O and l are still zero and need no rescaling.
+    auto rebase = [&](bool first) {
       float mt = scur[0][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
       mt = __builtin_fmaxf(mt, xor32(mt));
-      const float m_new = __builtin_fmaxf(m_run, mt * c);
-      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
-      m_run = m_new;
-      l_run *= alpha;
+      const float shift = (mt == -INFINITY) ? 0.f : mt;
+      m_ref += shift;
+      if (!first) {
+        const float alpha = fast_exp2(-shift);
+        l_run *= alpha;
 #pragma unroll
-      for (int vq = 0; vq < D / 32; ++vq)
+        for (int vq = 0; vq < D / 32; ++vq)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm[i] = -m_ref;
+      return shift;
     };
     auto softmax = [&]() {
       const int j0 = j * BN;
@@ -355,12 +376,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
             if (key >= N || (CAUSAL && key > qrow)) scur[kq][i] = -INFINITY;
           }
       }
-      if (j == 0) rebase();
-      float psum = exps((m_run == -INFINITY) ? 0.f : -m_run);
-      if (__builtin_amdgcn_ballot_w64(!(psum <= kOperandLimit)) != 0) {
-        rebase();
-        psum = exps((m_run == -INFINITY) ? 0.f : -m_run);
-      }
+      float psum;
+      if (j == 0) psum = exps(std::true_type{}, rebase(true));
+      else psum = exps(std::false_type{}, 0.f);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= kOperandLimit)) != 0)
+        psum = exps(std::true_type{}, rebase(false));
       l_run += psum;
     };
     if constexpr (lead) {
@@ -424,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   }
   if (qrow < N && p.lse != nullptr && hh == 0)
     p.lse[((long long)b * p.Hq + hq) * N + qrow] =
-        l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D, bool CAUSAL>
