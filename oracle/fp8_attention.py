@@ -12,14 +12,17 @@ Steps (the FP8 path's own, in order):
    scales (``quant.quantize``; Q and K optionally rotated with the same signs).
 2. Dequantise: Qd = code·sq, Kd = code·sk (fp64).
 3. S = scale · Qd·Kdᵀ, causal mask as in ``attention``; p = exp(S − m) with m
-   the row max; l = Σ p (unquantised).
+   the row max.
 4. The probabilities feed the second product in FP8.  The V block scale sv and
    a power-of-two headroom are folded into them before rounding:
        p̃_ij = e4m3(p_ij · sv(block j) · 2^8 / sv_max)
    with sv_max the largest V scale of that (batch, kv head), so p̃ <= 256.
    (The kernel rounds relative to its running max tile by tile; here the final
    row max is used, which is why this is a sanity reference only.)
-5. O = (Σ_j p̃_ij · v_code_j) · sv_max / 2^8 / l.
+5. The denominator sums the same rounded probabilities, mapped back by their
+   block's factor: l_i = Σ_j p̃_ij · sv_max / (sv(block j) · 2^8), so the weights
+   that divide are the weights that entered the second product.
+6. O = (Σ_j p̃_ij · v_code_j) · sv_max / 2^8 / l.
 """
 from __future__ import annotations
 
@@ -50,10 +53,10 @@ def fp8_attention_emul(q8, k8, v8, sq, sk, sv, scale=None, causal=False, rows=No
                 S = np.where(np.arange(N)[None, :] > rows[:, None], -np.inf, S)
             m = S.max(axis=1)
             p = np.exp(S - m[:, None])
-            l = p.sum(axis=1)
             svb = np.repeat(sv[b, kvh], BLOCK)[:N]
             svmax = sv[b, kvh].max()
             f = svb * 2.0 ** P_HEADROOM_LOG2 / svmax
             pq = e4m3.decode(e4m3.encode(p * f[None, :]))
+            l = (pq / f[None, :]).sum(axis=1)
             out[b, :, h, :] = (pq @ vcode[b, :, kvh, :]) * (svmax / 2.0 ** P_HEADROOM_LOG2) / l[:, None]
     return out

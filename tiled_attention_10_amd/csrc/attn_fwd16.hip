@@ -79,30 +79,8 @@ struct Geo {
   }
 };
 
-#ifndef TATTN_READ_AHEAD
-#define TATTN_READ_AHEAD 2
-#endif
 // Products between an LDS read and the product that consumes it.
-constexpr int kReadAhead = TATTN_READ_AHEAD;
-
-// Scheduling order of a stream of NPV P·V products (two transposing LDS reads
-// each) and NSC score products (one LDS read each): the reads of the first
-// kReadAhead products, then each product followed by the reads of the product
-// kReadAhead places later.
-template <int NPV, int NSC, int I = 0>
-__device__ inline void mma_stream_order() {
-  constexpr int N = NPV + NSC;
-  constexpr int A = kReadAhead < N ? kReadAhead : N;
-  if constexpr (I == 0) {
-    constexpr int lead_reads = 2 * (A < NPV ? A : NPV) + (A > NPV ? A - NPV : 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, lead_reads, 0);
-  }
-  if constexpr (I < N) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if constexpr (I + A < N) __builtin_amdgcn_sched_group_barrier(0x100, (I + A < NPV) ? 2 : 1, 0);
-    mma_stream_order<NPV, NSC, I + 1>();
-  }
-}
+constexpr int kReadAhead = 2;
 
 struct KernelParams {
   const uint16_t* q;
@@ -290,11 +268,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   // product that consumes it.
   auto pv_only = [&](const int vst) {
     pv(vst);
-    mma_stream_order<BN / 16 * (D / 32), 0>();
+    mma_read_order<BN / 16 * (D / 32), 2, kReadAhead>();
   };
   auto scores_only = [&](const int kst) {
     scores(kst, scur);
-    mma_stream_order<0, D / 8>();
+    mma_read_order<D / 8, 1, kReadAhead>();
   };
 
   if (lead && ntw > 0) scores_only(0);
@@ -350,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
-      mt = __builtin_fmaxf(mt, xor32(mt));
+      mt = max_xor32(mt);
       const float shift = (mt == -INFINITY) ? 0.f : mt;
       m_ref += shift;
       if (!first) {

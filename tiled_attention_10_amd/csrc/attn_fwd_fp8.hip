@@ -14,9 +14,10 @@
 //                   (rescale whenever a row max grows).
 //   Oᵀ += V8ᵀ·P̃ᵀ    P̃ = e4m3(p · sv(tile)·2^8/max(sv)): the V block scale and a
 //                   2^8 headroom are folded into the exponent bias, so p̃ <= 256
-//                   and small probabilities keep E4M3's precision; the denominator
-//                   accumulates the unrounded fp32 p.  A = Vᵀ gathered by
-//                   byte-transposing LDS reads (ds_read_b64_tr_b8, 4 per MFMA).
+//                   and small probabilities keep E4M3's precision.  The denominator
+//                   sums the same rounded P̃ with one more MFMA against an all-ones
+//                   operand, which gives every lane its row's tile sum.  A = Vᵀ
+//                   gathered by byte-transposing LDS reads (ds_read_b64_tr_b8, 4 per MFMA).
 // Epilogue: O = acc · max(sv)·2^-8 / z, rounded to the output type.
 #include <type_traits>
 
@@ -39,6 +40,7 @@ constexpr int TILEB = BN * ROWB;         // 8 KB
 constexpr int LDSB = 2 * STAGES * TILEB; // K ring + V ring
 constexpr float kHeadroomLog2 = 8.0f;
 constexpr int kMaxBlocks = 4096;         // scale blocks per head staged in LDS (N <= 262144)
+constexpr int kReadAhead = 2;            // products between an LDS read and its use
 
 // Physical 16-byte chunk = logical chunk ^ swz(row) (rows of 128 bytes).
 __device__ inline int swz(int r) {
@@ -77,7 +79,7 @@ template <typename OutT, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) {
   __shared__ __attribute__((aligned(1024))) char smem[LDSB];
   __shared__ float red[NW];
-  __shared__ float sk_lds[kMaxBlocks], sv_lds[kMaxBlocks];
+  __shared__ float sk_lds[kMaxBlocks], bias_lds[kMaxBlocks];
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
@@ -119,14 +121,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   }
   const float sq = p.qsc[((long long)b * p.Hq + hq) * p.nblk + qr / BN];
 
-  // Stage this head's K and V block scales in LDS (the loop then reads them with
-  // LDS loads, which do not wait on the K/V prefetch) and take the largest V scale.
+  // Stage this head's K block scales in LDS (the loop then reads them with LDS
+  // loads, which do not wait on the K/V prefetch), take the largest V scale, and
+  // stage each V block's exponent bias log2(sv/max sv) + 8.
   float vmax = 0.f;
   for (int i = tid; i < p.nblk; i += kThreads) {
-    const float sv = vsc[i];
     sk_lds[i] = ksc[i];
-    sv_lds[i] = sv;
-    vmax = fmaxf(vmax, sv);
+    vmax = fmaxf(vmax, vsc[i]);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off /= 2) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
@@ -135,6 +136,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   vmax = red[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) vmax = fmaxf(vmax, red[w]);
+  for (int i = tid; i < p.nblk; i += kThreads) bias_lds[i] = __log2f(vsc[i] / vmax) + kHeadroomLog2;
+  __syncthreads();
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;
@@ -146,12 +149,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   const int ld_col = 16 * ((lane & 7) ^ swz(ld_row));
   const uint32_t ld_off = (uint32_t)(ld_row * kvrow + ld_col);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  // Offsets for the last tile: rows past N repeat row N-1 (their probabilities are 0).
+  const int jl = (nt - 1) * BN;
+  const uint32_t ld_off_last = (uint32_t)((min(jl + ld_row, N - 1) - jl) * kvrow + ld_col);
+  // Tile t of K (ring 0) or V (ring 1) into ring stage ``stage``.  Tiles past the end
+  // repeat the last tile (into a stage nobody reads again), so every wave issues the
+  // same loads in every step and every address stays inside K and V.
   auto issue = [&](int ring, int stage, int t) {
-    const int j0 = t * BN;
-    const char* base = (ring ? vg : kg) + (long long)j0 * kvrow;
-    uint32_t off = ld_off;
-    if (j0 + BN > N) off = (uint32_t)((min(j0 + ld_row, N - 1) - j0) * kvrow + ld_col);   // rows past N repeat row N-1
-    lds_dma16(base, off, lds_base + (ring * STAGES + stage) * TILEB + 1024 * wave);
+    t = min(t, nt - 1);
+    const char* base = (ring ? vg : kg) + (long long)(t * BN) * kvrow;
+    lds_dma16(base, t == nt - 1 ? ld_off_last : ld_off, lds_base + (ring * STAGES + stage) * TILEB + 1024 * wave);
   };
 
   // K reads: row kr = perm23(l32) (+32 per key block), 16-byte chunks 4t + 2hh + u.
@@ -188,6 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
         s[kq] = mfma_fp8(a, qf[t], t == 0 ? f32x16{} : s[kq]);
       }
     }
+    mma_read_order<4, 2, kReadAhead>();
   };
 
   f32x16 oacc[D / 32];
@@ -195,35 +203,66 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float cq = p.c * sq;
+  f32x16 scur[2];   // raw scores of the tile whose softmax comes next
+  i32x8 pf;         // P̃ of the last softmax (operand of the next P·V)
+  // The two wave groups sharing each SIMD alternate between exponentials and
+  // matrix-core work ([FA3-V3] §7.3's ping-pong between warpgroups).  In step j:
+  //   group 0: softmax(j)              | P·V(j), scores(j+1)   (scores(0) in the prologue)
+  //   group 1: P·V(j-1), scores(j)     | softmax(j)            (P·V(last) after the loop)
   const bool lead = wave < NW / 2;
 
+  auto pv = [&](const int vst) {
+    const lds_char* vs = lds + vst * TILEB;   // voff carries the V ring base
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < nt) { issue(0, t, t); issue(1, t, t); }
+    for (int vq = 0; vq < D / 32; ++vq) {
+      const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq]));
+      const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq] + 16 * ROWB));
+      const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq] + 32 * ROWB));
+      const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq] + 48 * ROWB));
+      const i32x8 a = cat(__builtin_shufflevector(r0, r1, 0, 1, 2, 3), __builtin_shufflevector(r2, r3, 0, 1, 2, 3));
+      oacc[vq] = mfma_fp8(a, pf, oacc[vq]);
+    }
+    mma_read_order<D / 32, 4, kReadAhead>();
+  };
+
+  // Prologue: K tiles 0..2 and V tiles 0..1, then scores(0) for group 0.
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t) {
+    if (t < nt) issue(0, t, t);
+    if (t < STAGES - 2 && t < nt) issue(1, t, t);
+  }
   wait_vmcnt<0>();
   barrier();
-
-  f32x16 scur[2];
   if (lead && ntw > 0) scores(0, scur);
+  // Score scale and exponent bias of the tile whose softmax comes next, read from
+  // LDS a phase ahead of their use (group 0 for tile j+1 during step j, group 1 for
+  // tile j at the start of step j).
+  float cj_next = 0.f, bias_next = 0.f;
+  auto fetch_scales = [&](int t) {
+    t = min(t, nt - 1);
+    cj_next = cq * sk_lds[t];
+    bias_next = bias_lds[t];
+  };
+  if (lead) fetch_scales(0);
 
   auto step = [&](auto stc, auto leadc, int j) {
     constexpr int st = decltype(stc)::value;
     constexpr int stn = (st + 1) % STAGES;
+    constexpr int stp = (st + STAGES - 1) % STAGES;
     constexpr bool is_lead = decltype(leadc)::value;
-    if (j + 2 < nt) wait_vmcnt<2>();
-    else wait_vmcnt<0>();
+    // Needed now: K(j+1) and V(j), issued two steps ago; K(j+2) and V(j+1) may be in
+    // flight.  The barrier also retires every wave's reads of K(j-1) and V(j-2),
+    // whose stages receive K(j+3) and V(j+2) in this step.
+    wait_vmcnt<2>();
     barrier();
-    if (j + 3 < nt) {
-      issue(0, (st + 3) % STAGES, j + 3);
-      issue(1, (st + 3) % STAGES, j + 3);
-    }
-    if (j >= ntw) return;
+    // Loads go out at two points of each wave's schedule, which differ between the
+    // groups, so that the loads of eight waves do not queue in the address unit together.
+    auto load_k = [&]() { issue(0, (st + 3) % STAGES, j + 3); };
+    auto load_v = [&]() { issue(1, (st + 2) % STAGES, j + 2); };
 
-    i32x8 pf;
     auto softmax = [&]() {
       const int j0 = j * BN;
-      const float cj = cq * sk_lds[j];
-      const float bias = __log2f(sv_lds[j] / vmax) + kHeadroomLog2;
+      const float cj = cj_next, bias = bias_next;
       if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0)) {
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq)
@@ -238,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
       for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
-      mt = __builtin_fmaxf(mt, xor32(mt));
+      mt = max_xor32(mt);
       const float m_cand = mt * cj;
       if (__builtin_amdgcn_ballot_w64(m_cand > m_run) != 0) {
         const float m_new = __builtin_fmaxf(m_run, m_cand);
@@ -256,44 +295,40 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
       for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
         for (int i = 0; i < 16; ++i) pe[16 * kq + i] = fast_exp2(fmaf(scur[kq][i], cj, neg));
-      float ps[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ps[i] = pe[2 * i] + pe[2 * i + 1];
-#pragma unroll
-      for (int w = 8; w >= 1; w /= 2)
-#pragma unroll
-        for (int i = 0; i < w; ++i) ps[i] = ps[i] + ps[i + w];
-      l_run += ps[0] * fast_exp2(-bias);
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], 0, false);
         pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w + 2], pe[4 * w + 3], word, true);
       }
-    };
-    auto pv = [&]() {
-      const lds_char* vs = lds + st * TILEB;   // voff carries the V ring base
-#pragma unroll
-      for (int vq = 0; vq < D / 32; ++vq) {
-        const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq]));
-        const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq] + 16 * ROWB));
-        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq] + 32 * ROWB));
-        const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + voff[vq] + 48 * ROWB));
-        const i32x8 a = cat(__builtin_shufflevector(r0, r1, 0, 1, 2, 3), __builtin_shufflevector(r2, r3, 0, 1, 2, 3));
-        oacc[vq] = mfma_fp8(a, pf, oacc[vq]);
-      }
+      // Row sum of this tile's P̃: ones(32x64) · P̃ᵀ puts it in every element of the lane.
+      const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                          0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+      const f32x16 tsum = mfma_fp8(ones, pf, f32x16{});
+      l_run = fmaf(tsum[0], fast_exp2(-bias), l_run);
     };
     if constexpr (is_lead) {
+      if (j >= ntw) {
+        load_k();
+        load_v();
+        return;
+      }
       softmax();
       __builtin_amdgcn_sched_barrier(0);
-      pv();
-      __builtin_amdgcn_sched_barrier(0);
-      scores(stn, scur);
+      fetch_scales(j + 1);
+      load_k();
+      pv(st);
+      load_v();
+      if (j + 1 < ntw) scores(stn, scur);
     } else {
-      scores(st, scur);
+      const bool has_pv = j >= 1 && j - 1 < ntw, has_scores = j < ntw;
+      fetch_scales(j);
+      load_k();
+      if (has_pv) pv(stp);
+      load_v();
+      if (has_scores) scores(st, scur);
+      if (!has_scores) return;
       __builtin_amdgcn_sched_barrier(0);
       softmax();
-      __builtin_amdgcn_sched_barrier(0);
-      pv();
     }
   };
   auto run = [&](auto leadc) {
@@ -304,10 +339,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
       if (j + 3 < nt) step(std::integral_constant<int, 3>{}, leadc, j + 3);
     }
   };
-  if (lead) run(std::true_type{});
-  else run(std::false_type{});
+  if (lead) {
+    run(std::true_type{});
+  } else {
+    run(std::false_type{});
+    if (ntw == nt && nt > 0) pv((nt - 1) % STAGES);
+  }
+  wait_vmcnt<0>();   // the last steps' loads land in the rings reused below
 
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = l_run;   // both lanes of a row hold the full row sum
   const float inv = l_tot > 0.f ? vmax * 0.00390625f / l_tot : 0.f;   // max(sv)·2^-8 / z
   // The rings are free once every wave has left the loop; each wave stages its rows in 8 KB.
   __syncthreads();

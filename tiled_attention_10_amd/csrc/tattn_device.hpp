@@ -97,4 +97,15 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max(x, x of lane ^ 32) without an LDS round trip: v_permlane32_swap exchanges the
+// upper half of one register with the lower half of the other, leaving the lower
+// halves of x in both halves of ``lo`` and the upper halves in both halves of ``hi``.
+// The nops cover the VALU-write / permlane-read and permlane-write / VALU-read
+// hazards.  (The compiler builtin returns its first result for both outputs here.)
+__device__ inline float max_xor32(float x) {
+  float lo = x, hi = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+  return __builtin_fmaxf(lo, hi);
+}
+
 }  // namespace tattn

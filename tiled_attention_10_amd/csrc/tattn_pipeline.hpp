@@ -81,4 +81,19 @@ __device__ inline void store_rows(__attribute__((address_space(3))) char* stage,
   }
 }
 
+// Scheduling order of a stream of N matrix-core products that each consume R LDS
+// reads: the reads of the first A products, then each product followed by the
+// reads of the product A places later, so every read is issued A products ahead
+// of its use.  (Masks: 0x100 LDS read, 0x008 MFMA.)
+template <int N, int R, int A, int I = 0>
+__device__ inline void mma_read_order() {
+  constexpr int AA = A < N ? A : N;
+  if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, R * AA, 0);
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I + AA < N) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    mma_read_order<N, R, A, I + 1>();
+  }
+}
+
 }  // namespace tattn
