@@ -2,12 +2,13 @@
 // for gfx950.  Memory-bound: every element is read once and written once.
 //
 // One workgroup (4 waves) owns one (batch, head, block of 64 rows).  A row of
-// d channels is spread over d/8 lanes with 8 consecutive channels each, so a
-// row is one fully coalesced 16-byte-per-lane load.  The Walsh–Hadamard
-// butterflies with partner distance 1, 2, 4 run inside a lane; distances 8 ..
-// d/2 pair lanes whose chunk indices differ in one bit.  Stages run in
-// increasing distance with one fp32 add or subtract each, then one fp32
-// multiply by fl32(1/sqrt(d)), so the result is fully determined.
+// d channels is spread over 4 neighbouring lanes with d/4 consecutive channels
+// each (64 or 32 bytes per lane: coalesced 16-byte loads).  The Walsh–Hadamard
+// butterflies with partner distance 1 .. d/8 run inside a lane; the last two
+// (d/4, d/2) pair lanes 1 and 2 apart, exchanged with DPP quad permutes in the
+// VALU rather than through LDS.  Stages run in increasing distance with one fp32
+// add or subtract each, then one fp32 multiply by fl32(1/sqrt(d)), so the
+// result is fully determined.
 //
 // Quantisation ([FA3-V3] §4.3 per-block scales; the reading taken is
 // symmetric absmax with no offset): the block's absmax is reduced across the
@@ -31,85 +32,93 @@ struct RotParams {
   int N, H, nblk;
 };
 
+// Value of x in the lane whose index differs in bit ``ld`` (1 or 2) within its quad.
+template <int LD>
+__device__ inline float quad_xor(float x) {
+  constexpr int ctrl = LD == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
+}
+
 template <typename T, int D, bool ROT, bool QUANT>
 __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
-  constexpr int LPR = D / 8;          // lanes per row
-  constexpr int RPI = 64 / LPR;       // rows per wave per step
-  constexpr int STEPS = 16 / RPI;     // each wave covers 16 rows
+  constexpr int CPL = D / 4;          // channels per lane
+  constexpr int NV = CPL / 8;         // 16-byte loads per lane
   __shared__ float red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane % LPR, sub = lane / LPR;
+  const int li = lane & 3;
   const int blk = blockIdx.x % p.nblk;
   const int h = (blockIdx.x / p.nblk) % p.H;
   const int b = blockIdx.x / (p.nblk * p.H);
   const long long rs = (long long)p.H * D;     // elements between positions
-  const long long base = ((long long)b * p.N * p.H + h) * D + 8 * li;
+  const long long base = ((long long)b * p.N * p.H + h) * D + CPL * li;
+  const int row = blk * 64 + wave * 16 + (lane >> 2);
+  const bool valid = row < p.N;
 
-  uint32_t flip[8];
+  float y[CPL];
+  {
+    u32x4 raw[NV];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) flip[e] = (ROT && p.signs[8 * li + e] < 0) ? 0x80000000u : 0u;
-
-  float y[STEPS][8];
-  int rows[STEPS];
+    for (int v = 0; v < NV; ++v) raw[v] = valid ? *(const u32x4*)(p.x + base + row * rs + 8 * v) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
-    const int row = blk * 64 + wave * 16 + s * RPI + sub;
-    rows[s] = row;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (row < p.N) raw = *(const u32x4*)(p.x + base + row * rs);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t bits = (e & 1) ? (uint16_t)(raw[e / 2] >> 16) : (uint16_t)(raw[e / 2] & 0xffff);
-      y[s][e] = T::to_f32(bits);
+    for (int e = 0; e < CPL; ++e) {
+      const uint32_t w = raw[e / 8][(e % 8) / 2];
+      y[e] = T::to_f32((e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffff));
     }
-    if (ROT) {
+  }
+  if (ROT) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[s][e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, y[s][e]) ^ flip[e]);
+    for (int e = 0; e < CPL; ++e)
+      if (p.signs[CPL * li + e] < 0) y[e] = -y[e];
 #pragma unroll
-      for (int hd = 1; hd < 8; hd *= 2)
+    for (int hd = 1; hd < CPL; hd *= 2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!(e & hd)) {
-            const float a = y[s][e], c = y[s][e + hd];
-            y[s][e] = a + c;
-            y[s][e + hd] = a - c;
-          }
-#pragma unroll
-      for (int ld = 1; ld < LPR; ld *= 2) {
-        const bool upper = (li & ld) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float other = __shfl_xor(y[s][e], ld, 64);
-          y[s][e] = upper ? other - y[s][e] : y[s][e] + other;
+      for (int e = 0; e < CPL; ++e)
+        if (!(e & hd)) {
+          const float a = y[e], c = y[e + hd];
+          y[e] = a + c;
+          y[e + hd] = a - c;
         }
-      }
-      const float inv_sqrt_d = (D == 128) ? 0.08838834764831845f : 0.125f;
+    {
+      const bool upper = (li & 1) != 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        y[s][e] = y[s][e] * inv_sqrt_d;
-        // Keep the fp32 product: otherwise the multiply and the later 16-bit
-        // conversion fuse into one singly-rounded mixed-precision FMA.
-        __asm__ volatile("" : "+v"(y[s][e]));
+      for (int e = 0; e < CPL; ++e) {
+        const float other = quad_xor<1>(y[e]);
+        y[e] = upper ? other - y[e] : y[e] + other;
       }
+    }
+    {
+      const bool upper = (li & 2) != 0;
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const float other = quad_xor<2>(y[e]);
+        y[e] = upper ? other - y[e] : y[e] + other;
+      }
+    }
+    const float inv_sqrt_d = (D == 128) ? 0.08838834764831845f : 0.125f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      y[e] = y[e] * inv_sqrt_d;
+      // Keep the fp32 product: otherwise the multiply and the later 16-bit
+      // conversion fuse into one singly-rounded mixed-precision FMA.
+      __asm__ volatile("" : "+v"(y[e]));
     }
   }
 
   if constexpr (!QUANT) {
+    if (valid) {
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      if (rows[s] >= p.N) continue;
-      u32x4 w;
+      for (int v = 0; v < NV; ++v) {
+        u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack2<T>(y[s][2 * e], y[s][2 * e + 1]);
-      *(u32x4*)((uint16_t*)p.y + base + rows[s] * rs) = w;
+        for (int e = 0; e < 4; ++e) w[e] = pack2<T>(y[8 * v + 2 * e], y[8 * v + 2 * e + 1]);
+        *(u32x4*)((uint16_t*)p.y + base + row * rs + 8 * v) = w;
+      }
     }
   } else {
     float amax = 0.f;
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[s][e]));  // rows >= N hold zeros
+    for (int e = 0; e < CPL; ++e) amax = fmaxf(amax, fabsf(y[e]));   // rows >= N hold zeros
 #pragma unroll
     for (int off = 32; off >= 1; off /= 2) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     if (lane == 0) red[wave] = amax;
@@ -118,20 +127,20 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
     const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
     const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
     if (tid == 0) p.scales[((long long)b * p.H + h) * p.nblk + blk] = scale;
+    if (valid) {
+      uint32_t w[CPL / 4];
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      if (rows[s] >= p.N) continue;
-      u32x2 w;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int q = 0; q < CPL / 4; ++q) {
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(y[s][4 * half + e] * inv, -448.0f), 448.0f);
+        for (int e = 0; e < 4; ++e) v[e] = fminf(fmaxf(y[4 * q + e] * inv, -448.0f), 448.0f);
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
-        w[half] = (uint32_t)word;
+        w[q] = (uint32_t)word;
       }
-      *(u32x2*)((uint8_t*)p.y + base + rows[s] * rs) = w;
+      uint8_t* dst = (uint8_t*)p.y + base + row * rs;
+#pragma unroll
+      for (int v = 0; v < CPL / 16; ++v) *(u32x4*)(dst + 16 * v) = u32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]};
     }
   }
 }
