@@ -10,10 +10,11 @@
 //   scores          s = Sᵀ · sq(row block) · sk(tile) · scale·log2(e): per-block
 //                   scales ([FA3-V3] §4.3) applied in fp32; a 64-key tile is
 //                   exactly one K/V scale block.
-//   softmax         online, fp32 ([FA3-V3] §4.2); the running max is exact
-//                   (rescale whenever a row max grows).
+//   softmax         online, fp32 ([FA3-V3] §4.2); the reference max moves when
+//                   a row max passes it by more than kMaxSlack (log2 units), so
+//                   p <= 2^kMaxSlack and P̃ stays inside E4M3's range.
 //   Oᵀ += V8ᵀ·P̃ᵀ    P̃ = e4m3(p · sv(tile)·2^8/max(sv)): the V block scale and a
-//                   2^8 headroom are folded into the exponent bias, so p̃ <= 256
+//                   2^8 headroom are folded into the exponent bias, so p̃ < 448
 //                   and small probabilities keep E4M3's precision.  The denominator
 //                   sums the same rounded P̃ with one more MFMA against an all-ones
 //                   operand, which gives every lane its row's tile sum.  A = Vᵀ
@@ -39,6 +40,9 @@ constexpr int ROWB = D;                  // bytes per fp8 row
 constexpr int TILEB = BN * ROWB;         // 8 KB
 constexpr int LDSB = 2 * STAGES * TILEB; // K ring + V ring
 constexpr float kHeadroomLog2 = 8.0f;
+// How far a score may pass the reference max before it moves: with the 2^8
+// headroom, p̃ <= 2^(8 + kMaxSlack) = 445.7 < 448, the largest E4M3 value.
+constexpr float kMaxSlack = 0.8f;
 constexpr int kMaxBlocks = 4096;         // scale blocks per head staged in LDS (N <= 262144)
 constexpr int kReadAhead = 2;            // products between an LDS read and its use
 
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
       mt = max_xor32(mt);
       const float m_cand = mt * cj;
-      if (__builtin_amdgcn_ballot_w64(m_cand > m_run) != 0) {
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kMaxSlack) != 0) {
         const float m_new = __builtin_fmaxf(m_run, m_cand);
         const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
         m_run = m_new;
