@@ -137,6 +137,27 @@ def test_deterministic_and_gqa_equals_repeated_mha():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_move_the_reference_max(dtype, causal):
+    # Keys whose magnitude ramps along the sequence make a row's scores climb by
+    # ~65 in log2 units from the first tile to the last, so the kernel must move
+    # its reference max (and rescale O and z) several times: each move happens
+    # before a tile's probabilities could leave the 16-bit operand range.
+    rng = np.random.default_rng(77)
+    B, N, Hq, Hkv, d = 1, 700, 2, 1, 128
+    q = 1.0 + 0.1 * rng.standard_normal((B, N, Hq, d))
+    ramp = np.linspace(-1.0, 3.0, N)[None, :, None, None]
+    k = ramp + 0.1 * rng.standard_normal((B, N, Hkv, d))
+    v = rng.standard_normal((B, N, Hkv, d))
+    q, k, v = (W.to_torch(x.astype(np.float32), dtype) for x in (q, k, v))
+    o, lse = run(q, k, v, causal, lse=True)
+    ref, ref_lse = A.attention(q, k, v, None, causal, return_lse=True)
+    assert np.isfinite(o).all()
+    assert np.abs(o - ref).max() <= TOL[dtype]
+    assert (np.abs(lse - ref_lse) <= lse_tol(q, k, dtype) + 1e-6 * np.abs(ref_lse)).all()
+
+
 def test_scale_argument_is_used():
     q, k, v = (W.to_torch(x, "fp16") for x in W.random_qkv(33, 1, 200, 2, 2, 64))
     o = run(q, k, v, False, scale=0.37)
