@@ -322,14 +322,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
       load_k();
       pv(st);
       load_v();
-      if (j + 1 < ntw) scores(stn, scur);
+      scores(stn, scur);   // also on the wave's last tile (unused there): no branch, no copies
     } else {
       const bool has_pv = j >= 1 && j - 1 < ntw, has_scores = j < ntw;
       fetch_scales(j);
       load_k();
       if (has_pv) pv(stp);
       load_v();
-      if (has_scores) scores(st, scur);
+      scores(st, scur);   // also when unused, for the same reason
       if (!has_scores) return;
       __builtin_amdgcn_sched_barrier(0);
       softmax();
