@@ -206,6 +206,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  // Row sum of the last tile's P̃ (every element holds it) and its factor back to p
+  // units; added to l_run at the start of the next softmax, once the MFMA is long done.
+  f32x16 tsum = {};
+  float tfac = 0.f;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
   const float cq = p.c * sq;
   f32x16 scur[2];   // raw scores of the tile whose softmax comes next
   i32x8 pf;         // P̃ of the last softmax (operand of the next P·V)
@@ -276,6 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
             if (key >= N || (CAUSAL && key > qrow)) scur[kq][i] = -INFINITY;
           }
       }
+      l_run = fmaf(tsum[0], tfac, l_run);   // the previous tile's sum, before any rescale
       float mt = scur[0][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
@@ -301,14 +308,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
         for (int i = 0; i < 16; ++i) pe[16 * kq + i] = fast_exp2(fmaf(scur[kq][i], cj, neg));
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], 0, false);
+        // (the old-value operand is overwritten byte for byte; passing a source spares a move)
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], __builtin_bit_cast(int, pe[4 * w]), false);
         pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w + 2], pe[4 * w + 3], word, true);
       }
       // Row sum of this tile's P̃: ones(32x64) · P̃ᵀ puts it in every element of the lane.
-      const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                          0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
-      const f32x16 tsum = mfma_fp8(ones, pf, f32x16{});
-      l_run = fmaf(tsum[0], fast_exp2(-bias), l_run);
+      tsum = mfma_fp8(ones, pf, f32x16{});
+      tfac = fast_exp2(-bias);
     };
     if constexpr (is_lead) {
       if (j >= ntw) {
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   }
   wait_vmcnt<0>();   // the last steps' loads land in the rings reused below
 
-  const float l_tot = l_run;   // both lanes of a row hold the full row sum
+  const float l_tot = fmaf(tsum[0], tfac, l_run);   // both lanes of a row hold the full row sum
   const float inv = l_tot > 0.f ? vmax * 0.00390625f / l_tot : 0.f;   // max(sv)·2^-8 / z
   // The rings are free once every wave has left the loop; each wave stages its rows in 8 KB.
   __syncthreads();
