@@ -9,33 +9,35 @@
 //
 // Staging ([FA3-tile] §二's double buffer, generalised to four stages).  K and
 // V tiles go global -> LDS directly (16-byte LDS-DMA loads, no VGPR staging)
-// into four-stage rings.  While tile j is consumed, the loads for tiles j+2 and
-// j+3 are in flight; one barrier per tile both publishes the finished loads
-// (read after write) and retires the stage about to be overwritten (write after
-// read).  LDS rows are unpadded and their 16-byte chunks are XOR-
-// swizzled per row so that the K reads and the transposing V reads are free
-// of bank conflicts.
+// into four-stage rings; during step j the loads of K(j+3) and V(j+2) go out
+// while K(j+1) and V(j) are consumed.  One barrier per tile both publishes the
+// finished loads (read after write) and retires the stages about to be
+// overwritten (write after read).  LDS rows are unpadded and their 16-byte
+// chunks are XOR-swizzled per row so that the K reads and the transposing V
+// reads are free of bank conflicts.
 //
 // Per tile and wave, on the 32x32x16 matrix cores:
 //   Sᵀ = K·Qᵀ   A = K rows from LDS (rows taken in an order that swaps bits 2
-//                and 3 of the row index), B = Q.  Lane l then holds 32 scores
+//                and 3 of the row index), B = c·Q with c = scale·log2(e), so
+//                scores come out in log2 units.  The accumulator starts from
+//                −m_ref, the row's reference max.  Lane l then holds 32 scores
 //                of query row l%32: row statistics are lane-local apart from
 //                one exchange with lane l^32.
-//   softmax     online, fp32 ([FA3-V3] §4.2): m' = max(m, rowmax), α = 2^(m−m'),
-//                p = 2^(s·c − m') with c = scale·log2(e), z' = α·z + Σp.  The
-//                reference max is set on the first tile and only moves when a
-//                tile's probabilities would leave the 16-bit operand range, which
-//                skips the row max and the O rescale on almost every tile; O/z
-//                is unchanged in exact arithmetic.
+//   softmax     online, fp32 ([FA3-V3] §4.2): p = 2^(accumulator), one v_exp
+//                per element, z' = z + Σp.  The reference max is set on the first
+//                tile and only moves (by δ, with O and z scaled by 2^−δ) when a
+//                tile's probabilities would leave the 16-bit operand range,
+//                which skips the row max and the O rescale on almost every tile;
+//                O/z is unchanged in exact arithmetic.
 //   Oᵀ += Vᵀ·Pᵀ A = Vᵀ gathered by transposing LDS reads (ds_read_b64_tr_b16),
 //                B = P rounded to the input type.  Thanks to the K row order
 //                above, the score accumulator already is the B operand, so P
 //                needs no shuffle ([FA3-V3] §7.4's accumulator-to-operand
 //                problem, solved by operand order).
-// The loop is software-pipelined ([FA3-V3] §7.3's intra-warpgroup overlap):
-// tile j+1's score MFMAs are issued in the same basic block as tile j's
-// exponentials and P·V MFMAs, so matrix-core and VALU work of one wave
-// overlap; two waves per SIMD add overlap across waves.
+// Scheduling ([FA3-V3] §7.3's ping-pong, between the two waves of each SIMD):
+// a wave's VALU work does not overlap its own matrix-core work, so the two wave
+// groups alternate, one running its exponentials while the other issues its
+// products (see step() below).
 // The epilogue divides by z (deferred normalisation, [FA3-V3] §11) and writes
 // O and optionally the log-sum-exp.
 #include <type_traits>

@@ -21,20 +21,13 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One 16-byte LDS-DMA load per lane: lane i's 16 bytes from ``src`` land at LDS
-// byte address ``lds_addr`` + 16·i.  Issued as inline assembly so that the
-// compiler neither treats it as an aliasing LDS store (which would make it wait
-// for the load before every later LDS read) nor counts it: the kernels wait for
-// these loads explicitly with wait_vmcnt before each barrier.  M0 is only
-// written here and consumed by the next instruction.
-__device__ inline void lds_dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
-               : "memory");
-}
-
-// Same, with a wave-uniform base pointer and a 32-bit per-lane byte offset.
+// One 16-byte LDS-DMA load per lane: lane i's 16 bytes from ``base`` +
+// ``offset`` (wave-uniform base, 32-bit per-lane byte offset) land at LDS byte
+// address ``lds_addr`` + 16·i.  Issued as inline assembly so that the compiler
+// neither treats it as an aliasing LDS store (which would make it wait for the
+// load before every later LDS read) nor counts it: the kernels wait for these
+// loads explicitly with wait_vmcnt before each barrier.  M0 is only written here
+// and consumed by the next instruction.
 __device__ inline void lds_dma16(const void* base, uint32_t offset, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
