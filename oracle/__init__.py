@@ -29,6 +29,10 @@ Modules:
   random-sign rotation (pinned by orthogonality and invariance tests).
 * ``quant``      -- per-(batch, head, 64-row block) absmax scaling and e4m3
   codes, with the rounding decisions taken in fp32 (the kernel's precision).
+* ``rope``       -- rotary position embedding (half-split pairs, caller's cos/sin
+  tables) ahead of the rotation and quantiser: the fused prologue of
+  [FA3-card] "低精度优化" (pinned by tests/test_oracle_rope.py: identity,
+  norms, composition, complex form, relative position, planted sign error).
 * ``fp8_attention`` -- fp64 emulation of the fp8 attention path.  PARITY
   UNPINNED by the pages beyond their qualitative claim: it serves as a loose
   sanity bound, the criterion being RMSE against the exact fp64 result.
