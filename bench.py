@@ -11,10 +11,13 @@ With --dtype fp8 a step is attn_fwd_fp8 on E4M3 codes prepared once by
 hadamard_rotate (rotation + quantisation, timed separately as the prologue).
 
 Prints ONE JSON line: throughput in TFLOPS (4·N²·d·Hq·B per step, halved when
-causal), the attention kernel's roofline against the dense matrix-core peak,
+causal; mean over the timed steps, plus per-launch median and min), the
+attention kernel's roofline against the dense matrix-core peak,
 its HBM traffic when a counter measurement of the current kernel source is on
 record under profiles/, the fp8 leg on the same shape (unless --no-fp8 or
---dtype fp8), and the CPU oracle timed on a bounded row sample of the workload.
+--dtype fp8) with its HBM-bound prologue timed with and without the fused
+rotary embedding, and the CPU oracle timed on a bounded row sample of the
+workload.
 
 --copy-calibration runs only a plain device copy of known size (for scaling
 the FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exits.
@@ -112,6 +115,19 @@ def time_launches(torch, fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
 
 
+def launch_stats(torch, fn, n, stream):
+    """Median and min of n launches, each between its own pair of events (run after
+    the bracketed timing, so it does not change ``value``)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return round(t[len(t) // 2], 4), round(t[0], 4)
+
+
 def fp8_inputs(T, torch, W, w, q, k, v, dev):
     signs = torch.from_numpy(W.rotation_signs(w.wid, w.d)).to(dev)
     q8, sq = T.hadamard_rotate(q, signs, quantize=True)
@@ -123,7 +139,33 @@ def fp8_inputs(T, torch, W, w, q, k, v, dev):
         T.hadamard_rotate(k, signs, quantize=True, out=k8, scales=sk)
         T.hadamard_rotate(v, None, quantize=True, out=v8, scales=sv)
 
-    return (q8, k8, v8, sq, sk, sv), prologue
+    cos, sin = (torch.from_numpy(t).to(dev) for t in W.rotary_tables(w.wid, q.shape[1], q.shape[3]))
+
+    def prologue_rope():
+        # the same prologue with the rotary embedding of Q and K fused in
+        T.rope_hadamard_rotate(q, cos, sin, signs, quantize=True, out=q8, scales=sq)
+        T.rope_hadamard_rotate(k, cos, sin, signs, quantize=True, out=k8, scales=sk)
+        T.hadamard_rotate(v, None, quantize=True, out=v8, scales=sv)
+
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+
+    def prologue_rope_unfused():
+        # rotary embedding as a pass of its own (16-bit out), then the plain prologue
+        T.rope_hadamard_rotate(q, cos, sin, None, out=qr)
+        T.rope_hadamard_rotate(k, cos, sin, None, out=kr)
+        T.hadamard_rotate(qr, signs, quantize=True, out=q8, scales=sq)
+        T.hadamard_rotate(kr, signs, quantize=True, out=k8, scales=sk)
+        T.hadamard_rotate(v, None, quantize=True, out=v8, scales=sv)
+
+    return (q8, k8, v8, sq, sk, sv), prologue, (prologue_rope, prologue_rope_unfused)
+
+
+def prologue_bytes(q, k, v):
+    """HBM bytes of the fp8 prologue: 16-bit inputs read once, E4M3 codes and block
+    scales written once (the small rotary tables and signs not counted)."""
+    n = q.numel() + k.numel() + v.numel()
+    blocks = sum(t.shape[0] * t.shape[2] * ((t.shape[1] + 63) // 64) for t in (q, k, v))
+    return 2 * n + n + 4 * blocks
 
 
 def main():
@@ -161,17 +203,19 @@ def main():
 
     extra = {}
     if args.dtype == "fp8":
-        ins, prologue = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
+        ins, prologue, _ = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
         kernel = "attn_fwd_fp8_kernel"
-        ms, wall = time_launches(torch, lambda: T.attn_fwd_fp8(*ins, causal=causal, out=out),
-                                 args.steps, args.warmup, stream)
+        step_fn = lambda: T.attn_fwd_fp8(*ins, causal=causal, out=out)
+        ms, wall = time_launches(torch, step_fn, args.steps, args.warmup, stream)
+        extra["ms_median"], extra["ms_min"] = launch_stats(torch, step_fn, args.steps, stream)
         pms, _ = time_launches(torch, prologue, max(3, args.steps // 4), 5, stream)
         extra["prologue_ms"] = round(pms, 4)
         extra["with_prologue_tflops"] = round(flops / ((ms + pms) * 1e-3) / 1e12, 2)
     else:
         kernel = "attn_fwd16_kernel"
-        ms, wall = time_launches(torch, lambda: T.attn_fwd(qd, kd, vd, causal=causal, out=out),
-                                 args.steps, args.warmup, stream)
+        step_fn = lambda: T.attn_fwd(qd, kd, vd, causal=causal, out=out)
+        ms, wall = time_launches(torch, step_fn, args.steps, args.warmup, stream)
+        extra["ms_median"], extra["ms_min"] = launch_stats(torch, step_fn, args.steps, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.dtype]
 
@@ -197,11 +241,19 @@ def main():
     }
     res.update(extra)
     if args.dtype != "fp8" and not args.no_fp8 and w.d == 128:
-        ins, prologue = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
+        ins, prologue, prologue_rope = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
         out8 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
         fms, _ = time_launches(torch, lambda: T.attn_fwd_fp8(*ins, causal=causal, out=out8),
                                args.steps, args.warmup, stream)
-        pms, _ = time_launches(torch, prologue, 5, 2, stream)
+        pms, _ = time_launches(torch, prologue, 20, 10, stream)
+        prms, _ = time_launches(torch, prologue_rope[0], 20, 10, stream)
+        purms, _ = time_launches(torch, prologue_rope[1], 20, 10, stream)
+        pbytes = prologue_bytes(qd, kd, vd)
+        res["fp8_prologue"] = {"ms": round(pms, 4), "with_rope_ms": round(prms, 4),
+                               "with_rope_separate_pass_ms": round(purms, 4),
+                               "hbm_bytes": pbytes, "GB_per_s": round(pbytes / (pms * 1e-3) / 1e9, 1),
+                               "with_rope_GB_per_s": round(pbytes / (prms * 1e-3) / 1e9, 1),
+                               "frac_of_hbm_8TBps": round(pbytes / (pms * 1e-3) / 8e12, 4)}
         res["fp8"] = {"ms_per_step": round(fms, 4), "tflops": round(flops / (fms * 1e-3) / 1e12, 2),
                       "frac_of_fp8_peak": round(flops / (fms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                       "prologue_ms": round(pms, 4), "speedup_vs_" + args.dtype: round(ms / fms, 3),

@@ -82,8 +82,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * rotation); V must not be rotated.  Both products run on FP8 matrix cores with
  * fp32 accumulation; the scores' scales are applied in fp32; the probabilities
  * are rounded to E4M3 for the second product after multiplying them by
- * s_v(block) · 2^8 / max_blocks(s_v) (undone in fp32 in the epilogue), while
- * the softmax denominator accumulates the unrounded fp32 probabilities.
+ * s_v(block) · 2^8 / max_blocks(s_v) (undone in fp32 in the epilogue), and
+ * the softmax denominator sums those same rounded probabilities (mapped back
+ * by the same factor), so O is a weighted mean with the weights that entered
+ * the second product.
  *
  *   q8, k8, v8              codes as above (read); 16-byte aligned
  *   q_scale, k_scale, v_scale  fp32 [B, Hq|Hkv, ceil(N/64)], finite and > 0
@@ -125,6 +127,25 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  */
 int hadamard_rotate(const void* x, void* y, const int8_t* signs, float* scales_out,
                     int B, int N, int H, int d, int in_dtype, void* stream);
+
+/*
+ * rope_hadamard_rotate — hadamard_rotate() with a rotary position embedding
+ * applied first, in the same pass over memory ([FA3-card] "低精度优化": the
+ * Hadamard rotation is memory bound and can be fused with the rotary
+ * embedding at no extra cost).  The pages do not define the embedding; it is
+ * the standard rotation of channel pairs (i, i + d/2), i < d/2, of the row at
+ * position n by the caller's angle θ[n, i]:
+ *     r_i       = fl(fl(x_i · cos) − fl(x_{i+d/2} · sin))
+ *     r_{i+d/2} = fl(fl(x_{i+d/2} · cos) + fl(x_i · sin))      (fp32, no fused ops)
+ * and then exactly hadamard_rotate() on r (rotation if signs != NULL, FP8
+ * block quantisation if scales_out != NULL, else output in in_dtype).
+ *
+ *   rope_cos, rope_sin   fp32 [N, d/2] (row n = position n), 16-byte aligned (read)
+ *   other arguments as for hadamard_rotate.
+ */
+int rope_hadamard_rotate(const void* x, void* y, const float* rope_cos, const float* rope_sin,
+                         const int8_t* signs, float* scales_out, int B, int N, int H, int d,
+                         int in_dtype, void* stream);
 
 /* Text for a status code (static storage). */
 const char* tattn_status_string(int status);

@@ -34,7 +34,8 @@ def L():
 
 def test_header_declares_the_three_operations():
     fns = declared_functions()
-    for name in ("attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "tattn_status_string", "tattn_last_error"):
+    for name in ("attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "tattn_status_string",
+                 "tattn_last_error"):
         assert name in fns
 
 
@@ -95,6 +96,20 @@ def rot(L, x=P, y=P, signs=None, scales=None, B=1, N=64, H=1, d=128, dtype=2):
 ])
 def test_hadamard_rotate_rejects(L, kw, status):
     assert rot(L, **kw) == status
+
+
+def rope_rot(L, x=P, y=P, cos=P, sin=P, signs=None, scales=None, B=1, N=64, H=1, d=128, dtype=2):
+    return L.rope_hadamard_rotate(x, y, cos, sin, signs, scales, B, N, H, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cos=None), INVALID), (dict(sin=None), INVALID), (dict(cos=P + 4), MISALIGNED),
+    (dict(sin=P + 8), MISALIGNED), (dict(x=None), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(dtype=9), UNSUPPORTED), (dict(N=0), INVALID), (dict(y=BAD), MISALIGNED),
+])
+def test_rope_hadamard_rotate_rejects(L, kw, status):
+    assert rope_rot(L, **kw) == status
+    assert L.tattn_last_error() != b""
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch):

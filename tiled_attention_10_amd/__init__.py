@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_fp8.restype = i
         L.hadamard_rotate.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
         L.hadamard_rotate.restype = i
+        L.rope_hadamard_rotate.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+        L.rope_hadamard_rotate.restype = i
         L.tattn_status_string.argtypes = [i]
         L.tattn_status_string.restype = ctypes.c_char_p
         L.tattn_last_error.argtypes = []
@@ -181,4 +183,30 @@ def hadamard_rotate(x, signs=None, quantize: bool = False, out=None, scales=None
         scales = None
     _check(lib().hadamard_rotate(_ptr(x), _ptr(out), _ptr(signs), _ptr(scales), B, N, H, d, code,
                                  _stream(dev)))
+    return (out, scales) if quantize else out
+
+
+def rope_hadamard_rotate(x, rope_cos, rope_sin, signs=None, quantize: bool = False, out=None, scales=None):
+    """Rotary embedding of x [B, N, H, d] by the fp32 tables rope_cos/rope_sin [N, d/2]
+    (channel pairs (i, i + d/2)), then exactly ``hadamard_rotate`` in the same pass."""
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be [B, N, H, d]")
+    B, N, H, d = x.shape
+    code = _dtype_code(x.dtype)
+    for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (N, d // 2) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 [{N}, {d // 2}]")
+    if signs is not None:
+        if signs.dtype != torch.int8 or tuple(signs.shape) != (d,):
+            raise ValueError(f"signs must be int8 [{d}]")
+    dev = _dev(x, rope_cos, rope_sin, signs)
+    if quantize:
+        out = _out(out, (B, N, H, d), torch.uint8, dev, "out")
+        scales = _out(scales, (B, H, (N + 63) // 64), torch.float32, dev, "scales")
+    else:
+        out = _out(out, (B, N, H, d), x.dtype, dev, "out")
+        scales = None
+    _check(lib().rope_hadamard_rotate(_ptr(x), _ptr(out), _ptr(rope_cos), _ptr(rope_sin), _ptr(signs),
+                                      _ptr(scales), B, N, H, d, code, _stream(dev)))
     return (out, scales) if quantize else out

@@ -48,6 +48,22 @@ int hip_status(hipError_t e, const char* what) {
   return fail(TATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
+int rotate_common(const void* x, void* y, const float* rope_cos, const float* rope_sin, const int8_t* signs,
+                  float* scales_out, int B, int N, int H, int d, int in_dtype, void* stream) {
+  if (!x || !y) return fail(TATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (int s = check_shape(B, N, H, H, d)) return s;
+  if (d != 64 && d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (in_dtype != TATTN_F16 && in_dtype != TATTN_BF16)
+    return fail(TATTN_ERR_UNSUPPORTED, "in_dtype %d", in_dtype);
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TATTN_ERR_MISALIGNED, "x, y must be 16-byte aligned");
+  if (scales_out && !aligned(scales_out, 4)) return fail(TATTN_ERR_MISALIGNED, "scales_out must be 4-byte aligned");
+  tattn::RotateArgs a{};
+  a.x = x; a.y = y; a.signs = signs; a.scales = scales_out;
+  a.rope_cos = rope_cos; a.rope_sin = rope_sin;
+  a.B = B; a.N = N; a.H = H; a.d = d; a.dtype = in_dtype;
+  return hip_status(tattn::launch_hadamard_rotate(a, (hipStream_t)stream), "rotation launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,20 +128,21 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const 
   return hip_status(tattn::launch_attn_fwd_fp8(a, (hipStream_t)stream), "attn_fwd_fp8 launch");
 }
 
+
 int hadamard_rotate(const void* x, void* y, const int8_t* signs, float* scales_out, int B, int N,
                     int H, int d, int in_dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (!x || !y) return fail(TATTN_ERR_INVALID_ARG, "null tensor pointer");
-  if (int s = check_shape(B, N, H, H, d)) return s;
-  if (d != 64 && d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
-  if (in_dtype != TATTN_F16 && in_dtype != TATTN_BF16)
-    return fail(TATTN_ERR_UNSUPPORTED, "in_dtype %d", in_dtype);
-  if (!aligned(x, 16) || !aligned(y, 16)) return fail(TATTN_ERR_MISALIGNED, "x, y must be 16-byte aligned");
-  if (scales_out && !aligned(scales_out, 4)) return fail(TATTN_ERR_MISALIGNED, "scales_out must be 4-byte aligned");
-  tattn::RotateArgs a{};
-  a.x = x; a.y = y; a.signs = signs; a.scales = scales_out;
-  a.B = B; a.N = N; a.H = H; a.d = d; a.dtype = in_dtype;
-  return hip_status(tattn::launch_hadamard_rotate(a, (hipStream_t)stream), "hadamard_rotate launch");
+  return rotate_common(x, y, nullptr, nullptr, signs, scales_out, B, N, H, d, in_dtype, stream);
+}
+
+int rope_hadamard_rotate(const void* x, void* y, const float* rope_cos, const float* rope_sin,
+                         const int8_t* signs, float* scales_out, int B, int N, int H, int d,
+                         int in_dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!rope_cos || !rope_sin) return fail(TATTN_ERR_INVALID_ARG, "null rotary table");
+  if (!aligned(rope_cos, 16) || !aligned(rope_sin, 16))
+    return fail(TATTN_ERR_MISALIGNED, "rotary tables must be 16-byte aligned");
+  return rotate_common(x, y, rope_cos, rope_sin, signs, scales_out, B, N, H, d, in_dtype, stream);
 }
 
 }  // extern "C"

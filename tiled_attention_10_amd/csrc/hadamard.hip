@@ -10,6 +10,11 @@
 // add or subtract each, then one fp32 multiply by fl32(1/sqrt(d)), so the
 // result is fully determined.
 //
+// Rotary embedding (optional, before everything else; [FA3-card] "低精度优化"
+// names it as fusable with the rotation): the partner of channel i is i ± d/2,
+// which sits in the lane two places away in the same quad (d/4 channels per
+// lane), so one more DPP exchange and two fp32 products per element suffice.
+//
 // Quantisation ([FA3-V3] §4.3 per-block scales; the reading taken is
 // symmetric absmax with no offset): the block's absmax is reduced across the
 // workgroup, scale = absmax/448 and inv = 448/absmax are IEEE fp32 divisions,
@@ -29,6 +34,8 @@ struct RotParams {
   void* y;
   const int8_t* signs;
   float* scales;
+  const float* rcos;
+  const float* rsin;
   int N, H, nblk;
 };
 
@@ -39,7 +46,7 @@ __device__ inline float quad_xor(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
 }
 
-template <typename T, int D, bool ROT, bool QUANT>
+template <typename T, int D, bool ROT, bool QUANT, bool ROPE>
 __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
   constexpr int CPL = D / 4;          // channels per lane
   constexpr int NV = CPL / 8;         // 16-byte loads per lane
@@ -64,6 +71,28 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
     for (int e = 0; e < CPL; ++e) {
       const uint32_t w = raw[e / 8][(e % 8) / 2];
       y[e] = T::to_f32((e & 1) ? (uint16_t)(w >> 16) : (uint16_t)(w & 0xffff));
+    }
+  }
+  if (ROPE) {
+    // lanes 0, 1 of a quad hold channels [0, d/2), lanes 2, 3 their partners
+    const long long t = (long long)min(row, p.N - 1) * (D / 2) + CPL * (li & 1);
+    float c[CPL], sn[CPL];
+#pragma unroll
+    for (int v = 0; v < CPL / 4; ++v) {
+      const f32x4 cv = *(const f32x4*)(p.rcos + t + 4 * v);
+      const f32x4 sv = *(const f32x4*)(p.rsin + t + 4 * v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[4 * v + e] = cv[e];
+        sn[4 * v + e] = sv[e];
+      }
+    }
+    const bool second = (li & 2) != 0;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const float other = quad_xor<2>(y[e]);
+      const float a = y[e] * c[e], b = other * sn[e];
+      y[e] = second ? a + b : a - b;
     }
   }
   if (ROT) {
@@ -145,6 +174,16 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
   }
 }
 
+template <typename T, int D, bool ROPE>
+hipError_t launch_dr(const RotParams& p, dim3 grid, bool rot, bool q, hipStream_t stream) {
+  const dim3 block(256);
+  if (rot && q) hipLaunchKernelGGL((hadamard_kernel<T, D, true, true, ROPE>), grid, block, 0, stream, p);
+  else if (rot) hipLaunchKernelGGL((hadamard_kernel<T, D, true, false, ROPE>), grid, block, 0, stream, p);
+  else if (q) hipLaunchKernelGGL((hadamard_kernel<T, D, false, true, ROPE>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((hadamard_kernel<T, D, false, false, ROPE>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_d(const RotateArgs& a, hipStream_t stream) {
   RotParams p;
@@ -152,16 +191,15 @@ hipError_t launch_d(const RotateArgs& a, hipStream_t stream) {
   p.y = a.y;
   p.signs = a.signs;
   p.scales = a.scales;
+  p.rcos = a.rope_cos;
+  p.rsin = a.rope_sin;
   p.N = a.N;
   p.H = a.H;
   p.nblk = (a.N + 63) / 64;
-  const dim3 grid((unsigned)((long long)p.nblk * a.H * a.B)), block(256);
+  const dim3 grid((unsigned)((long long)p.nblk * a.H * a.B));
   const bool rot = a.signs != nullptr, q = a.scales != nullptr;
-  if (rot && q) hipLaunchKernelGGL((hadamard_kernel<T, D, true, true>), grid, block, 0, stream, p);
-  else if (rot) hipLaunchKernelGGL((hadamard_kernel<T, D, true, false>), grid, block, 0, stream, p);
-  else if (q) hipLaunchKernelGGL((hadamard_kernel<T, D, false, true>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((hadamard_kernel<T, D, false, false>), grid, block, 0, stream, p);
-  return hipGetLastError();
+  if (a.rope_cos != nullptr) return launch_dr<T, D, true>(p, grid, rot, q, stream);
+  return launch_dr<T, D, false>(p, grid, rot, q, stream);
 }
 
 template <typename T>

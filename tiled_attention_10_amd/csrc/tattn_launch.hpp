@@ -27,6 +27,8 @@ struct RotateArgs {
   void* y;
   const int8_t* signs;
   float* scales;
+  const float* rope_cos;   // rotary tables [N, d/2] or NULL (no rotary embedding)
+  const float* rope_sin;
   int B, N, H, d;
   int dtype;
 };

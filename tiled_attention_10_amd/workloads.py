@@ -5,7 +5,8 @@ rounds them to the storage dtype.  Every tensor is laid out [B, N, H, d].
 
 Recipe: ``np.random.default_rng([workload_id, tensor_id])`` draws standard
 normals in fp32 (tensor 0 = Q, 1 = K, 2 = V, 3 = rotation signs, 4 = outlier
-channels); the values are then rounded to nearest-even into fp16 or bf16.  The
+channels, 5 = rotary angles); the values are then rounded to nearest-even into
+fp16 or bf16.  The
 FP8 workload first multiplies one seeded channel per head of Q and K by 20
 (0.5 % of d = 128 channels rounds up to one channel per head).
 
@@ -73,6 +74,13 @@ def normal(wid: int, tensor: int, shape) -> np.ndarray:
 def rotation_signs(wid: int, d: int) -> np.ndarray:
     """Seeded ±1 vector (int8) of length d."""
     return np.where(_rng(wid, 3).integers(0, 2, size=d) == 1, 1, -1).astype(np.int8)
+
+
+def rotary_tables(wid: int, N: int, d: int):
+    """Seeded rotary tables: cos and sin (fp32 [N, d/2]) of angles drawn uniformly
+    in [-pi, pi) (tensor 5).  Any angles are valid inputs of the rotary step."""
+    ang = _rng(wid, 5).uniform(-np.pi, np.pi, size=(N, d // 2))
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 def outlier_channels(wid: int, H: int, d: int) -> np.ndarray:
