@@ -4,9 +4,13 @@
  * C ABI.  Plain pointers and sizes only.  Every tensor is a dense row-major
  * array laid out [B, N, H, d] (batch, sequence position, head, channel) in
  * device memory that the caller allocates and owns; the library allocates
- * nothing and keeps no mutable global state, so calls from several host
- * threads are safe.  Every call is asynchronous on ``stream`` (a hipStream_t;
- * NULL means the default stream) and returns before the GPU has finished.
+ * nothing, and its only global state is a per-device cache of the compute-unit
+ * count (written atomically), so calls from several host threads are safe.
+ * Every call is asynchronous on ``stream`` (a hipStream_t; NULL means the
+ * default stream) and returns before the GPU has finished.  The attention
+ * kernels launch one workgroup per compute unit of the current device and each
+ * workgroup walks a fixed share of the work; running them beside other kernels
+ * on the same device is correct but may serialise part of the grid.
  *
  * Return value: TATTN_OK (0) or one of the TATTN_ERR_* codes below.  Argument
  * checks run on the host before any HIP call, so a rejected call touches

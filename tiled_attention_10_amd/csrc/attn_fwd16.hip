@@ -1,11 +1,16 @@
 // Fused attention forward, fp16/bf16, for gfx950 (CDNA4).
 //
-// Work decomposition.  One workgroup = 8 waves = BM = 256 query rows of one
-// (batch, head); each wave owns 32 rows and keeps its Q rows in VGPRs for the
-// whole sequence.  The K/V sequence is walked in tiles of BN = 64 keys.  Work
-// items are ordered (batch, head, q tile) and dealt so that consecutive items
-// land on one XCD, which keeps the heads of a KV group (and all q tiles of a
-// head) on one L2.  Causal launches take the longest rows first.
+// Work decomposition.  A q tile = BM = 256 query rows of one (batch, head),
+// processed by one workgroup of 8 waves; each wave owns 32 rows and keeps its Q
+// rows in VGPRs for the whole sequence.  The K/V sequence is walked in tiles of
+// BN = 64 keys.  The grid is persistent, one workgroup per CU (the 128 KB of LDS
+// admit no second one), and each workgroup walks an equal share of the items:
+// the hardware then dispatches only once, where handing out q tiles of unequal
+// cost one by one left CUs idle between them.  Items are ordered (batch, head,
+// q tile) and dealt so that each XCD takes one contiguous range, which keeps the
+// heads of a KV group (and all q tiles of a head) on one L2.  A causal item is
+// the pair of q tiles nqt-1-r and r (heavy first), which costs nqt + 1 tile
+// rows whatever r is, so the static shares are balanced.
 //
 // Staging ([FA3-tile] §二's double buffer, generalised to four stages).  K and
 // V tiles go global -> LDS directly (16-byte LDS-DMA loads, no VGPR staging)
@@ -91,7 +96,10 @@ struct KernelParams {
   uint16_t* o;
   float* lse;
   int N, Hq, Hkv, group, nqt;
-  float c;  // scale · log2(e)
+  int nper;     // work items per (batch, head): q tiles, or causal pairs of q tiles
+  int nitems;   // nper · Hq · B
+  int remap;    // deal items so that each XCD gets a contiguous range (needs 8 | nitems, 8 | grid)
+  float c;      // scale · log2(e)
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -104,16 +112,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
 
-  const int Gn = gridDim.x;
-  const int g = blockIdx.x;
-  const int wi = (Gn % 8 == 0) ? (g % 8) * (Gn / 8) + g / 8 : g;
-  int qt = wi % p.nqt;
-  if (CAUSAL) qt = p.nqt - 1 - qt;
-  const int rest = wi / p.nqt;
+  // Persistent: the grid holds one workgroup per CU and each walks its share of
+  // the items; item v runs on XCD v % 8, and with ``remap`` the XCD's items form
+  // one contiguous range of (batch, head), so a KV group stays in one L2.
+  // Causal items pair q tile nqt-1-r with q tile r: every pair costs nqt + 1
+  // units of 256 keys, so equal shares balance without a queue.
+  for (int v = blockIdx.x; v < p.nitems; v += gridDim.x) {
+  const int wi = p.remap ? (v % 8) * (p.nitems / 8) + v / 8 : v;
+  const int r = wi % p.nper;
+  const int rest = wi / p.nper;
+  const int nsub = (CAUSAL && r != p.nqt - 1 - r) ? 2 : 1;
+  for (int sub = 0; sub < nsub; ++sub) {
+  const int qt = CAUSAL ? (sub == 0 ? p.nqt - 1 - r : r) : r;
+  // Opaque per item: lane-derived offsets are recomputed for each item instead of
+  // being hoisted out of the item loop and kept live through the tile loop.
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, hh = lane >> 5;
   const int hq = rest % p.Hq;
   const int b = rest / p.Hq;
   const int hkv = hq / p.group;
@@ -209,7 +226,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
       }
   }
 
-  f32x16 scur[2];   // scores of the tile whose softmax comes next, minus m_ref
+  // Defined per item: left undefined, they would be carried from the last item.
+  f32x16 scur[2] = {f32x16{}, f32x16{}};   // scores of the tile whose softmax comes next, minus m_ref
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
@@ -239,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   // so each wave's softmax runs while the other wave of its SIMD issues both of
   // its products.  Step j reads K(j), K(j+1), V(j-1) and V(j).
   const bool lead = wave < NW / 2;
-  vec8 pf[BN / 16];   // probabilities of the last softmax (operand of the next P·V)
+  vec8 pf[BN / 16] = {};   // probabilities of the last softmax (operand of the next P·V)
 
   // Prologue: K tiles 0..2 and V tiles 0..1, then scores(0) for group 0.
 #pragma unroll
@@ -425,6 +443,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   if (qrow < N && p.lse != nullptr && hh == 0)
     p.lse[((long long)b * p.Hq + hq) * N + qrow] =
         l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // The next item's first loads overwrite the staging blocks of other waves.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier();
+  }
+  }
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -440,8 +463,11 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.group = a.Hq / a.Hkv;
   p.nqt = (a.N + BM - 1) / BM;
+  p.nper = CAUSAL ? (p.nqt + 1) / 2 : p.nqt;
+  p.nitems = p.nper * a.Hq * a.B;
   p.c = (float)((double)a.scale * 1.4426950408889634);
-  const long long grid = (long long)p.nqt * a.Hq * a.B;
+  const int grid = p.nitems < device_cu_count() ? p.nitems : device_cu_count();
+  p.remap = (p.nitems % 8 == 0 && grid % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd16_kernel<T, D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();

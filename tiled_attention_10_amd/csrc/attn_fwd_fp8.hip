@@ -76,7 +76,10 @@ struct Fp8Params {
   uint16_t* o;
   float* lse;
   int N, Hq, Hkv, group, nqt, nblk;
-  float c;  // softmax scale · log2(e)
+  int nper;     // work items per (batch, head): q tiles, or causal pairs of q tiles
+  int nitems;   // nper · Hq · B
+  int remap;    // deal items so that each XCD gets a contiguous range (needs 8 | nitems, 8 | grid)
+  float c;      // softmax scale · log2(e)
 };
 
 template <typename OutT, bool CAUSAL>
@@ -87,16 +90,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   lds_char* const lds = (lds_char*)smem;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
 
-  const int Gn = gridDim.x;
-  const int g = blockIdx.x;
-  const int wi = (Gn % 8 == 0) ? (g % 8) * (Gn / 8) + g / 8 : g;
-  int qt = wi % p.nqt;
-  if (CAUSAL) qt = p.nqt - 1 - qt;
-  const int rest = wi / p.nqt;
+  // Persistent: one workgroup per CU walks its share of the items (the same
+  // dealing as the 16-bit kernel: XCD-contiguous ranges, causal q tiles paired
+  // nqt-1-r with r so that every item costs the same).
+  for (int v = blockIdx.x; v < p.nitems; v += gridDim.x) {
+  const int wi = p.remap ? (v % 8) * (p.nitems / 8) + v / 8 : v;
+  const int r = wi % p.nper;
+  const int rest = wi / p.nper;
+  const int nsub = (CAUSAL && r != p.nqt - 1 - r) ? 2 : 1;
+  for (int sub = 0; sub < nsub; ++sub) {
+  const int qt = CAUSAL ? (sub == 0 ? p.nqt - 1 - r : r) : r;
+  // Opaque per item: lane-derived offsets are recomputed for each item instead of
+  // being hoisted out of the item loop and kept live through the tile loop.
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, hh = lane >> 5;
   const int hq = rest % p.Hq;
   const int b = rest / p.Hq;
   const int hkv = hq / p.group;
@@ -213,8 +223,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
   const float cq = p.c * sq;
-  f32x16 scur[2];   // raw scores of the tile whose softmax comes next
-  i32x8 pf;         // P̃ of the last softmax (operand of the next P·V)
+  // Defined per item: left undefined, they would be carried from the last item.
+  f32x16 scur[2] = {f32x16{}, f32x16{}};   // raw scores of the tile whose softmax comes next
+  i32x8 pf = {};    // P̃ of the last softmax (operand of the next P·V)
   // The two wave groups sharing each SIMD alternate between exponentials and
   // matrix-core work ([FA3-V3] §7.3's ping-pong between warpgroups).  In step j:
   //   group 0: softmax(j)              | P·V(j), scores(j+1)   (scores(0) in the prologue)
@@ -366,6 +377,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
   if (qrow < N && p.lse != nullptr && hh == 0)
     p.lse[((long long)b * p.Hq + hq) * N + qrow] =
         l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // The next item's first loads and scale tables overwrite LDS that other waves
+  // may still be reading.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier();
+  }
+  }
 }
 
 template <typename OutT, bool CAUSAL>
@@ -385,8 +402,11 @@ hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
   p.group = a.Hq / a.Hkv;
   p.nqt = (a.N + BM - 1) / BM;
   p.nblk = (a.N + BN - 1) / BN;
+  p.nper = CAUSAL ? (p.nqt + 1) / 2 : p.nqt;
+  p.nitems = p.nper * a.Hq * a.B;
   p.c = (float)((double)a.scale * 1.4426950408889634);
-  const long long grid = (long long)p.nqt * a.Hq * a.B;
+  const int grid = p.nitems < device_cu_count() ? p.nitems : device_cu_count();
+  p.remap = (p.nitems % 8 == 0 && grid % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<OutT, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, p);
   return hipGetLastError();

@@ -33,6 +33,10 @@ struct RotateArgs {
   int dtype;
 };
 
+// Compute units of the current device (cached per device); persistent grids hold
+// one workgroup per CU.
+int device_cu_count();
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_attn_fwd16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_fp8(const AttnArgs& a, hipStream_t stream);
