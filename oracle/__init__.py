@@ -33,6 +33,10 @@ Modules:
   tables) ahead of the rotation and quantiser: the fused prologue of
   [FA3-card] "低精度优化" (pinned by tests/test_oracle_rope.py: identity,
   norms, composition, complex form, relative position, planted sign error).
+* ``decode``     -- one decode step over an FP8 block-quantised KV cache: the
+  fp64 definition on the dequantised cache, per-sequence lengths, GQA
+  (pinned by tests/test_oracle_decode.py: brute force, the causal prefill
+  oracle's last row, torch float64 SDPA, block-boundary and planted mistakes).
 * ``fp8_attention`` -- fp64 emulation of the fp8 attention path.  PARITY
   UNPINNED by the pages beyond their qualitative claim: it serves as a loose
   sanity bound, the criterion being RMSE against the exact fp64 result.

@@ -10,6 +10,12 @@ fp16 or bf16.  The
 FP8 workload first multiplies one seeded channel per head of Q and K by 20
 (0.5 % of d = 128 channels rounds up to one channel per head).
 
+Decode workloads draw the query from tensor 0, each sequence's K and V cache
+rows from the streams [workload_id, 1, b] and [workload_id, 2, b], and the
+sequence lengths (a mix between Nmax/2 and Nmax, the last one full) from
+tensor 6; the cache is stored as E4M3 codes with 64-row block scales, made by
+the block quantiser from these values.
+
 The workloads follow the shapes the pages discuss: the tiny single-head check,
 multi-head fp16 (the B=2, N=2048, d=128 benchmark of the FA3 deep-dive page,
 widened to 4 × 16 heads), one layer of a 70B-class model with grouped KV heads,
@@ -61,6 +67,60 @@ WORKLOADS = {
 }
 
 HEADLINE = "gqa_bf16_h64kv8_n8192"       # run non-causal for the headline figure
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: B sequences, each with one new query token [B, Hq, d]
+    attending to its own cached K/V [B, Nmax, Hkv, d] (the first seqlens[b] rows)."""
+    name: str
+    wid: int
+    B: int
+    Nmax: int
+    Hq: int
+    Hkv: int
+    d: int
+    dtype: str          # storage dtype of the query and the output
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def seqlens(self) -> np.ndarray:
+        """Length mix: uniform integers in [Nmax/2, Nmax] (tensor 6), the last
+        sequence full; int32 [B]."""
+        L = _rng(self.wid, 6).integers(self.Nmax // 2, self.Nmax + 1, size=self.B)
+        L[-1] = self.Nmax
+        return L.astype(np.int32)
+
+    def hbm_bytes(self, seqlens) -> int:
+        """Bytes a decode step must move at least: the valid cache rows (one byte
+        per K and V element), their block scales, the query and the output."""
+        rows = int(np.sum(np.asarray(seqlens, dtype=np.int64)))
+        blocks = int(np.sum((np.asarray(seqlens, dtype=np.int64) + 63) // 64))
+        return rows * self.Hkv * self.d * 2 + blocks * self.Hkv * 4 * 2 + 2 * self.B * self.Hq * self.d * 2
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DecodeWorkload("decode_fp8kv_b3_h8kv2_n1000", 6, 3, 1000, 8, 2, 128, "bf16"),
+        DecodeWorkload("decode_fp8kv_b4_h64kv8_n131072", 7, 4, 131072, 64, 8, 128, "bf16"),
+    ]
+}
+
+
+def decode_query_f32(w: DecodeWorkload) -> np.ndarray:
+    """fp32 query [B, Hq, d] of a decode workload (tensor 0)."""
+    return normal(w.wid, 0, (w.B, w.Hq, w.d))
+
+
+def decode_cache_f32(w: DecodeWorkload, b: int):
+    """fp32 K and V cache rows [Nmax, Hkv, d] of sequence b (tensors 1 and 2, one
+    stream per sequence so a sequence is drawn without the others)."""
+    k = np.random.default_rng([w.wid, 1, b]).standard_normal(size=(w.Nmax, w.Hkv, w.d), dtype=np.float32)
+    v = np.random.default_rng([w.wid, 2, b]).standard_normal(size=(w.Nmax, w.Hkv, w.d), dtype=np.float32)
+    return k, v
 
 
 def _rng(wid: int, tensor: int) -> np.random.Generator:
