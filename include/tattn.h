@@ -28,6 +28,7 @@
 #ifndef TATTN_H
 #define TATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -150,6 +151,57 @@ int hadamard_rotate(const void* x, void* y, const int8_t* signs, float* scales_o
 int rope_hadamard_rotate(const void* x, void* y, const float* rope_cos, const float* rope_sin,
                          const int8_t* signs, float* scales_out, int B, int N, int H, int d,
                          int in_dtype, void* stream);
+
+/*
+ * attn_decode_fp8kv — one decode step: each sequence's new query token attends
+ * to the keys and values cached for that sequence so far, stored as FP8 with
+ * per-block scales.
+ *
+ * The operation is [FA3-V3] §2's attention with a single query row per
+ * (sequence, query head); the cache format is §4.3's block quantisation (the
+ * layout hadamard_rotate() writes with signs = NULL and non-NULL scales_out).
+ * [FA3-tile]'s opening discusses this autoregressive setting at 128k-1M
+ * tokens, where memory bandwidth sets the speed; [FA3-V3] §5 lists FP8 KV
+ * caches among the deployment options.  For sequence b with L = seqlens[b]
+ * cached rows, query head h and KV head h / (Hq/Hkv):
+ *     k_j = e4m3(k_cache[b, j, kv, :]) · k_scale[b, kv, j/64]   (j < L; same for v_j)
+ *     s_j = softmax_scale · q[b, h, :]·k_j
+ *     O[b, h, :] = Σ_j softmax(s)_j · v_j,   lse[b, h] = log Σ_j e^(s_j)
+ * Computed in chunks of the sequence with the online-softmax merge of
+ * [FA3-V3] §4.2 (m = max(m_a, m_b), z = z_a·e^(m_a−m) + z_b·e^(m_b−m)), fp32
+ * statistics and accumulators; the products run on the matrix cores in the
+ * query's 16-bit type (E4M3 values convert to it exactly) and the
+ * probabilities are rounded to that type, times the V block scale over the
+ * largest V block scale of the keys a wave covers, before the second product.
+ *
+ *   q            [B, Hq, d] dtype (read)
+ *   k_cache      uint8 E4M3FN codes [B, Nmax, Hkv, d] (read; rows >= L unused)
+ *   v_cache      likewise
+ *   k_scale      fp32 [B, Hkv, ceil(Nmax/64)], finite and > 0 (read)
+ *   v_scale      likewise
+ *   seqlens      int32 [B] in DEVICE memory; values are clamped to [0, Nmax]
+ *                (1 <= L <= Nmax is the meaningful range; L = 0 gives O = 0 and
+ *                lse = -inf)
+ *   o            [B, Hq, d] dtype (written)
+ *   lse          fp32 [B, Hq] natural log, or NULL
+ *   workspace    device scratch owned by the caller, at least
+ *                attn_decode_fp8kv_workspace_size(B, Nmax, Hq, Hkv, d) bytes,
+ *                16-byte aligned; overwritten by the call, so calls that overlap
+ *                in time need separate workspaces
+ *   B, Nmax, Hq, Hkv >= 1, Hq % Hkv == 0, Hkv <= 65536, d = 128,
+ *   dtype TATTN_BF16 or TATTN_F16 (the type of q and o).
+ * Errors: TATTN_ERR_INVALID_ARG also for a workspace smaller than required.
+ */
+int attn_decode_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* seqlens,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      int B, int Nmax, int Hq, int Hkv, int d, float softmax_scale,
+                      int dtype, void* stream);
+
+/* Workspace bytes attn_decode_fp8kv needs for these sizes (0 if they are invalid).
+ * It depends on the sizes only (B·Hq·ceil(Nmax/chunk)·(d+2)·4 bytes, the chunk a
+ * function of B, Nmax, Hq, Hkv). */
+size_t attn_decode_fp8kv_workspace_size(int B, int Nmax, int Hq, int Hkv, int d);
 
 /* Text for a status code (static storage). */
 const char* tattn_status_string(int status);

@@ -34,8 +34,8 @@ def L():
 
 def test_header_declares_the_three_operations():
     fns = declared_functions()
-    for name in ("attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "tattn_status_string",
-                 "tattn_last_error"):
+    for name in ("attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "attn_decode_fp8kv",
+                 "attn_decode_fp8kv_workspace_size", "tattn_status_string", "tattn_last_error"):
         assert name in fns
 
 
@@ -110,6 +110,42 @@ def rope_rot(L, x=P, y=P, cos=P, sin=P, signs=None, scales=None, B=1, N=64, H=1,
 def test_rope_hadamard_rotate_rejects(L, kw, status):
     assert rope_rot(L, **kw) == status
     assert L.tattn_last_error() != b""
+
+
+def decode(L, q=P, kc=P, vc=P, ks=P, vs=P, sl=P, o=P, lse=None, ws=P, wsb=1 << 30, B=2, Nmax=1000, Hq=8, Hkv=2,
+           d=128, scale=0.1, dtype=2):
+    return L.attn_decode_fp8kv(q, kc, vc, ks, vs, sl, o, lse, ws, wsb, B, Nmax, Hq, Hkv, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(vs=None), INVALID), (dict(sl=None), INVALID),
+    (dict(o=None), INVALID), (dict(ws=None), INVALID), (dict(B=0), INVALID), (dict(Nmax=0), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID), (dict(Hkv=0), INVALID), (dict(d=64), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED),
+    (dict(scale=0.0), INVALID), (dict(scale=float("inf")), INVALID), (dict(q=BAD), MISALIGNED),
+    (dict(vc=P + 4), MISALIGNED), (dict(ws=P + 8), MISALIGNED), (dict(ks=P + 2), MISALIGNED),
+    (dict(sl=P + 1), MISALIGNED), (dict(lse=P + 3), MISALIGNED), (dict(wsb=16), INVALID),
+    (dict(B=1 << 20, Nmax=1 << 20, Hq=64, Hkv=8), INVALID),
+])
+def test_attn_decode_fp8kv_rejects(L, kw, status):
+    assert decode(L, **kw) == status
+    assert L.tattn_last_error() != b""
+
+
+def test_decode_workspace_size(L):
+    f = L.attn_decode_fp8kv_workspace_size
+    # B·Hq·ceil(Nmax/chunk)·(d + 2)·4 bytes; the chunk is a multiple of 256 keys
+    n = f(2, 1000, 8, 2, 128)
+    assert n > 0 and n % (2 * 8 * 130 * 4) == 0 and n // (2 * 8 * 130 * 4) == 4   # chunk 256
+    big = f(4, 131072, 64, 8, 128)
+    nc = big // (4 * 64 * 130 * 4)
+    assert big % (4 * 64 * 130 * 4) == 0 and 131072 % nc == 0 and (131072 // nc) % 256 == 0
+    for bad in ((0, 10, 8, 2, 128), (1, 10, 8, 3, 128), (1, 10, 8, 2, 64), (1, 0, 8, 2, 128)):
+        assert f(*bad) == 0
+    # the Python binding hands over exactly this size
+    assert T.decode_workspace_size(2, 1000, 8, 2, 128) == n
+    # a workspace one byte short of it is rejected before any HIP call
+    assert decode(L, wsb=n - 1) == INVALID
+    assert b"workspace" in L.tattn_last_error()
 
 
 def test_python_binding_fails_loudly_without_library(monkeypatch):

@@ -1,0 +1,217 @@
+"""GPU parity of attn_decode_fp8kv (through the C ABI) against the fp64 decode oracle.
+
+The cache is an input of the step: each side quantises the same 16-bit K and V
+values itself (the oracle with ``oracle.quant``, the GPU with hadamard_rotate's
+block quantiser), the codes and scales are checked to be identical, and the
+GPU output is compared with the oracle's exact attention over the dequantised
+cache.  The codes-only case draws the codes themselves so that every finite
+E4M3 value occurs.
+
+Tolerance, from the kernel's arithmetic (u = unit roundoff of the query's type:
+2^-8 bf16, 2^-11 fp16): the probabilities are rounded to that type and the
+denominator sums the same rounded values, so the output is a weighted mean
+whose weights are each within a relative 2u of the exact softmax; the output is
+then rounded once.  Per element
+    |ΔO| <= 1.01·u·|O| + (2.01·u + 1e-4)·max_j |v_j| + 1e-6
+(1e-4 covers the fp32 scores and exponentials), and on the seeded normal
+workloads also the method's 16-bit tolerances max|ΔO| <= 1e-2 (bf16) /
+2e-3 (fp16) on top of the output rounding.  The log-sum-exp sums the same
+rounded probabilities: |ΔLSE| <= u + 1e-5·(1 + |LSE|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import tiled_attention_10_amd as T
+from oracle import decode as D
+from oracle import quant
+from tiled_attention_10_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
+TOL = {"bf16": 1e-2, "fp16": 2e-3}
+TDT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def gpu_quantise(x16):
+    """[B, N, H, d] 16-bit torch (CPU) -> GPU codes and scales (block quantiser, no rotation)."""
+    c, s = T.hadamard_rotate(x16.to(DEV), None, quantize=True)
+    return c, s
+
+
+def run_gpu(q16, kc, ks, vc, vs, seqlens, scale=None):
+    B, Hq, d = q16.shape
+    print(f"[attn_decode_fp8kv] q{tuple(q16.shape)} cache{tuple(kc.shape)} seqlens={list(seqlens)[:8]}",
+          flush=True)
+    t = lambda x: x if isinstance(x, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(x))
+    sl = torch.tensor(np.asarray(seqlens, dtype=np.int32), device=DEV)
+    o, lse = T.attn_decode_fp8kv(t(q16).to(DEV), t(kc).to(DEV), t(vc).to(DEV), t(ks).to(DEV), t(vs).to(DEV),
+                                 sl, softmax_scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def vmax_per_head(vc, vs, seqlens, Hq):
+    """max_j |v_j| over each (b, query head)'s valid rows, from the oracle's dequantisation."""
+    V = np.abs(D.dequantize(vc, vs))                 # [B, N, Hkv, d]
+    B, _, Hkv, _ = V.shape
+    g = Hq // Hkv
+    out = np.zeros((B, Hq))
+    for b in range(B):
+        L = int(seqlens[b])
+        if L > 0:
+            m = V[b, :L].max(axis=(0, 2))            # [Hkv]
+            out[b] = np.repeat(m, g)
+    return out
+
+
+def check(o, lse, ref, ref_lse, vmax, dtype, natural=True, lens=None):
+    u = U[dtype]
+    err = np.abs(o - ref)
+    bound = 1.01 * u * np.abs(ref) + (2.01 * u + 1e-4) * vmax[..., None] + 1e-6
+    print(f"{dtype}: max|dO| {err.max():.3e}, worst fraction of the bound {(err / bound).max():.3f}, "
+          f"max|dLSE| {np.abs(lse - ref_lse)[np.isfinite(ref_lse)].max() if np.isfinite(ref_lse).any() else 0:.3e}")
+    assert np.isfinite(o).all()
+    assert (err <= bound).all()
+    if natural:
+        assert (err <= TOL[dtype] + 1.01 * u * np.abs(ref)).all()
+    fin = np.isfinite(ref_lse)
+    assert (np.abs(lse[fin] - ref_lse[fin]) <= u + 1e-5 * (1 + np.abs(ref_lse[fin]))).all()
+    assert np.array_equal(np.isfinite(lse), fin)
+
+
+def case(seed, B, Nmax, Hq, Hkv, seqlens, dtype, scale=None):
+    """Seeded normal q, K, V (16-bit), cache quantised on both sides; full comparison."""
+    q, k, v = W.random_qkv(seed, B, 1, Hq, Hkv, 128, Nk=Nmax)
+    q16 = W.to_torch(q[:, 0], dtype)
+    k16, v16 = W.to_torch(k, dtype), W.to_torch(v, dtype)
+    kc, ks = quant.quantize(k16.float().numpy())
+    vc, vs = quant.quantize(v16.float().numpy())
+    kg, ksg = gpu_quantise(k16)
+    vg, vsg = gpu_quantise(v16)
+    assert np.array_equal(kg.cpu().numpy(), kc) and np.array_equal(ksg.cpu().numpy(), ks)
+    assert np.array_equal(vg.cpu().numpy(), vc) and np.array_equal(vsg.cpu().numpy(), vs)
+    o, lse = run_gpu(q16, kg, ksg, vg, vsg, seqlens, scale)
+    ref, ref_lse = D.decode_attention(q16.float().numpy(), kc, ks, vc, vs, seqlens, scale, return_lse=True)
+    check(o, lse, ref, ref_lse, vmax_per_head(vc, vs, seqlens, Hq), dtype)
+    return o
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_decode_small_workload(dtype):
+    w = W.DECODE_WORKLOADS["decode_fp8kv_b3_h8kv2_n1000"]
+    q = W.decode_query_f32(w)
+    k = np.stack([W.decode_cache_f32(w, b)[0] for b in range(w.B)])
+    v = np.stack([W.decode_cache_f32(w, b)[1] for b in range(w.B)])
+    seqlens = w.seqlens()
+    q16, k16, v16 = W.to_torch(q, dtype), W.to_torch(k, dtype), W.to_torch(v, dtype)
+    kc, ks = quant.quantize(k16.float().numpy())
+    vc, vs = quant.quantize(v16.float().numpy())
+    kg, ksg = gpu_quantise(k16)
+    vg, vsg = gpu_quantise(v16)
+    assert np.array_equal(kg.cpu().numpy(), kc) and np.array_equal(vsg.cpu().numpy(), vs)
+    o, lse = run_gpu(q16, kg, ksg, vg, vsg, seqlens)
+    ref, ref_lse = D.decode_attention(q16.float().numpy(), kc, ks, vc, vs, seqlens, return_lse=True)
+    check(o, lse, ref, ref_lse, vmax_per_head(vc, vs, seqlens, w.Hq), dtype)
+
+
+def test_decode_ragged_lengths():
+    # lengths around the step (32 keys), block (64) and per-wave range (64 at the 256-key chunk)
+    case(11, 8, 700, 4, 4, [1, 2, 31, 33, 64, 65, 257, 700], "bf16")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (24, 1), (5, 1), (32, 2), (3, 3)])
+def test_decode_group_sizes(Hq, Hkv):
+    # 16 query heads fill one product; 24 needs two head groups, the second partly empty
+    case(20 + Hq, 2, 600, Hq, Hkv, [600, 377], "bf16")
+
+
+def test_decode_many_chunks():
+    # 79 chunks of 256 keys per sequence, merged by the second kernel
+    case(31, 2, 20000, 8, 1, [12345, 20000], "bf16")
+
+
+def test_decode_fp16_softmax_scale():
+    case(32, 3, 900, 8, 2, [900, 1, 450], "fp16", scale=0.3)
+
+
+def test_decode_every_code():
+    B, N, Hq, Hkv = 2, 2048, 8, 2
+    kc, ks = W.random_e4m3_cache(1, B, N, Hkv, 128)
+    vc, vs = W.random_e4m3_cache(2, B, N, Hkv, 128)
+    assert np.unique(kc).size == 254
+    q16 = W.to_torch(W.random_qkv(33, B, 1, Hq, Hkv, 128)[0][:, 0], "bf16")
+    seqlens = [2048, 1500]
+    o, lse = run_gpu(q16, kc, ks, vc, vs, seqlens)
+    ref, ref_lse = D.decode_attention(q16.float().numpy(), kc, ks, vc, vs, seqlens, return_lse=True)
+    check(o, lse, ref, ref_lse, vmax_per_head(vc, vs, seqlens, Hq), "bf16", natural=False)
+
+
+def test_decode_single_row_and_empty_sequence():
+    # L = 1: O is the dequantised v_0 rounded once; L = 0: O = 0 and LSE = -inf
+    B, N, Hq, Hkv = 3, 256, 4, 2
+    kc, ks = W.random_e4m3_cache(3, B, N, Hkv, 128)
+    vc, vs = W.random_e4m3_cache(4, B, N, Hkv, 128)
+    q16 = W.to_torch(W.random_qkv(34, B, 1, Hq, Hkv, 128)[0][:, 0], "bf16")
+    o, lse = run_gpu(q16, kc, ks, vc, vs, [1, 0, 256])
+    v0 = D.dequantize(vc, vs)[0, 0]                                   # [Hkv, d]
+    exp0 = torch.from_numpy(np.repeat(v0, Hq // Hkv, axis=0).astype(np.float32)).bfloat16().float().numpy()
+    assert np.array_equal(o[0], exp0)
+    assert np.array_equal(o[1], np.zeros_like(o[1])) and np.all(lse[1] == -np.inf)
+    ref, ref_lse = D.decode_attention(q16.float().numpy()[2:], kc[2:], ks[2:], vc[2:], vs[2:], [256],
+                                      return_lse=True)
+    check(o[2:], lse[2:], ref, ref_lse, vmax_per_head(vc[2:], vs[2:], [256], Hq), "bf16", natural=False)
+
+
+def test_decode_deterministic_and_workspace_reuse():
+    B, N, Hq, Hkv = 2, 3000, 16, 2
+    kc, ks = W.random_e4m3_cache(5, B, N, Hkv, 128)
+    vc, vs = W.random_e4m3_cache(6, B, N, Hkv, 128)
+    q = W.to_torch(W.random_qkv(35, B, 1, Hq, Hkv, 128)[0][:, 0], "bf16").to(DEV)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    ws = torch.empty(T.decode_workspace_size(B, N, Hq, Hkv, 128), dtype=torch.uint8, device=DEV)
+    sl = torch.tensor([3000, 2999], dtype=torch.int32, device=DEV)
+    o1 = T.attn_decode_fp8kv(q, t(kc), t(vc), t(ks), t(vs), sl, workspace=ws)
+    ws.fill_(0xFF)                                   # stale partials must not leak into the next call
+    o2 = T.attn_decode_fp8kv(q, t(kc), t(vc), t(ks), t(vs), sl, workspace=ws)
+    sl_short = torch.tensor([700, 10], dtype=torch.int32, device=DEV)
+    o3 = T.attn_decode_fp8kv(q, t(kc), t(vc), t(ks), t(vs), sl_short, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    ref = D.decode_attention(q.float().cpu().numpy(), kc, ks, vc, vs, [700, 10])
+    err = np.abs(o3.float().cpu().numpy() - ref)
+    assert err.max() <= 2.01 * 2 ** -8 * np.abs(D.dequantize(vc, vs)).max() + 1.01 * 2 ** -8 * np.abs(ref).max()
+
+
+def test_decode_full_size_sampled():
+    """The 128k-token workload (B=4, 64 query heads over 8 KV heads) in the benchmark's launch
+    configuration; the oracle checks two (sequence, KV head) slices, 8 query heads each."""
+    w = W.DECODE_WORKLOADS["decode_fp8kv_b4_h64kv8_n131072"]
+    seqlens = w.seqlens()
+    q16 = W.to_torch(W.decode_query_f32(w), "bf16")
+    kc = torch.empty((w.B, w.Nmax, w.Hkv, w.d), dtype=torch.uint8, device=DEV)
+    vc = torch.empty_like(kc)
+    nb = (w.Nmax + 63) // 64
+    ks = torch.empty((w.B, w.Hkv, nb), dtype=torch.float32, device=DEV)
+    vs = torch.empty_like(ks)
+    host = {}
+    for b in range(w.B):
+        kf, vf = W.decode_cache_f32(w, b)
+        k16, v16 = W.to_torch(kf[None], "bf16"), W.to_torch(vf[None], "bf16")
+        T.hadamard_rotate(k16.to(DEV), None, quantize=True, out=kc[b:b + 1], scales=ks[b:b + 1])
+        T.hadamard_rotate(v16.to(DEV), None, quantize=True, out=vc[b:b + 1], scales=vs[b:b + 1])
+        host[b] = (k16, v16)
+    torch.cuda.synchronize()
+    o, lse = run_gpu(q16, kc, ks, vc, vs, seqlens)
+    g = w.Hq // w.Hkv
+    for b, kv in ((0, 3), (w.B - 1, w.Hkv - 1)):
+        k16, v16 = host[b]
+        kcs, kss = quant.quantize(k16[:, :, kv:kv + 1].float().numpy())
+        vcs, vss = quant.quantize(v16[:, :, kv:kv + 1].float().numpy())
+        assert np.array_equal(kc[b:b + 1, :, kv:kv + 1].cpu().numpy(), kcs)
+        assert np.array_equal(vs[b:b + 1, kv:kv + 1].cpu().numpy(), vss)
+        qs = q16[b:b + 1, kv * g:(kv + 1) * g].float().numpy()
+        ref, ref_lse = D.decode_attention(qs, kcs, kss, vcs, vss, [int(seqlens[b])], return_lse=True)
+        check(o[b:b + 1, kv * g:(kv + 1) * g], lse[b:b + 1, kv * g:(kv + 1) * g], ref, ref_lse,
+              vmax_per_head(vcs, vss, [int(seqlens[b])], g), "bf16")

@@ -12,8 +12,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "TattnError", "lib", "LIB_PATH",
-           "TATTN_F16", "TATTN_BF16"]
+__all__ = ["attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "attn_decode_fp8kv",
+           "decode_workspace_size", "TattnError", "lib", "LIB_PATH", "TATTN_F16", "TATTN_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtattn.so")
 
@@ -46,6 +46,11 @@ def lib() -> ctypes.CDLL:
         L.hadamard_rotate.restype = i
         L.rope_hadamard_rotate.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
         L.rope_hadamard_rotate.restype = i
+        L.attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                         i, i, i, i, i, f, i, vp]
+        L.attn_decode_fp8kv.restype = i
+        L.attn_decode_fp8kv_workspace_size.argtypes = [i, i, i, i, i]
+        L.attn_decode_fp8kv_workspace_size.restype = ctypes.c_size_t
         L.tattn_status_string.argtypes = [i]
         L.tattn_status_string.restype = ctypes.c_char_p
         L.tattn_last_error.argtypes = []
@@ -210,3 +215,48 @@ def rope_hadamard_rotate(x, rope_cos, rope_sin, signs=None, quantize: bool = Fal
     _check(lib().rope_hadamard_rotate(_ptr(x), _ptr(out), _ptr(rope_cos), _ptr(rope_sin), _ptr(signs),
                                       _ptr(scales), B, N, H, d, code, _stream(dev)))
     return (out, scales) if quantize else out
+
+
+def decode_workspace_size(B: int, Nmax: int, Hq: int, Hkv: int, d: int) -> int:
+    """Bytes of device workspace ``attn_decode_fp8kv`` needs (0 for invalid sizes)."""
+    return int(lib().attn_decode_fp8kv_workspace_size(B, Nmax, Hq, Hkv, d))
+
+
+def attn_decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, seqlens, softmax_scale: float | None = None,
+                      out=None, return_lse: bool = False, lse=None, workspace=None):
+    """One decode step: q [B, Hq, d] (fp16/bf16) against an E4M3 KV cache (uint8 [B, Nmax, Hkv, d],
+    fp32 block scales [B, Hkv, ceil(Nmax/64)]) holding seqlens[b] (int32, on the device) rows per
+    sequence.  Returns O [B, Hq, d] in q's dtype (and LSE [B, Hq], fp32).  ``workspace`` is a
+    uint8 device tensor of at least ``decode_workspace_size`` bytes (allocated here if None)."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and the caches [B, Nmax, Hkv, d]")
+    B, Hq, d = q.shape
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}, v {tuple(v_cache.shape)}")
+    Nmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    for t in (k_cache, v_cache):
+        if t.dtype != torch.uint8:
+            raise TypeError("caches must be uint8 E4M3FN codes")
+    nb = (Nmax + 63) // 64
+    for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, Hkv, nb):
+            raise ValueError(f"{name} must be float32 {(B, Hkv, nb)}")
+    if seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,):
+        raise ValueError(f"seqlens must be int32 [{B}]")
+    code = _dtype_code(q.dtype)
+    dev = _dev(q, k_cache, v_cache, k_scale, v_scale, seqlens)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = _out(out, (B, Hq, d), q.dtype, dev, "out")
+    if return_lse or lse is not None:
+        lse = _out(lse, (B, Hq), torch.float32, dev, "lse")
+    need = decode_workspace_size(B, Nmax, Hq, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _dev(workspace)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().attn_decode_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                   _ptr(seqlens), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
+                                   B, Nmax, Hq, Hkv, d, scale, code, _stream(dev)))
+    return (out, lse) if lse is not None else out

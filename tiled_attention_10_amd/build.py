@@ -22,7 +22,7 @@ ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
-SOURCES = ["attn_fwd16.hip", "attn_fwd_fp8.hip", "hadamard.hip", "api.cpp"]
+SOURCES = ["attn_fwd16.hip", "attn_fwd_fp8.hip", "attn_decode.hip", "hadamard.hip", "api.cpp"]
 
 
 def _hipcc() -> str:

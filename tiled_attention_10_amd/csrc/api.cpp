@@ -163,4 +163,42 @@ int rope_hadamard_rotate(const void* x, void* y, const float* rope_cos, const fl
   return rotate_common(x, y, rope_cos, rope_sin, signs, scales_out, B, N, H, d, in_dtype, stream);
 }
 
+size_t attn_decode_fp8kv_workspace_size(int B, int Nmax, int Hq, int Hkv, int d) {
+  if (B < 1 || Nmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d != 128) return 0;
+  if (too_large(B, Nmax, Hq, d) || too_large(B, Nmax, Hkv, d)) return 0;
+  return tattn::plan_decode(B, Nmax, Hq, Hkv).ws_bytes;
+}
+
+int attn_decode_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_cache, const float* k_scale,
+                      const float* v_scale, const int32_t* seqlens, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int Nmax, int Hq, int Hkv, int d, float softmax_scale,
+                      int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !seqlens || !o || !workspace)
+    return fail(TATTN_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || Nmax < 1 || Hq < 1 || Hkv < 1)
+    return fail(TATTN_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d Nmax=%d Hq=%d Hkv=%d)", B, Nmax, Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(TATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (the decode path supports 128)", d);
+  if (dtype != TATTN_F16 && dtype != TATTN_BF16) return fail(TATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (too_large(B, Nmax, Hq, d) || too_large(B, Nmax, Hkv, d) || Hkv > 65536 || B > 65535)
+    return fail(TATTN_ERR_INVALID_ARG, "sizes too large (B=%d Nmax=%d Hq=%d Hkv=%d)", B, Nmax, Hq, Hkv);
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(TATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(workspace, 16))
+    return fail(TATTN_ERR_MISALIGNED, "q, caches, o and workspace must be 16-byte aligned");
+  if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(seqlens, 4) || (lse && !aligned(lse, 4)))
+    return fail(TATTN_ERR_MISALIGNED, "scales, seqlens and lse must be 4-byte aligned");
+  const tattn::DecodePlan pl = tattn::plan_decode(B, Nmax, Hq, Hkv);
+  if ((long long)Hkv * pl.nhg > 65535) return fail(TATTN_ERR_INVALID_ARG, "too many head groups");
+  if (workspace_bytes < pl.ws_bytes)
+    return fail(TATTN_ERR_INVALID_ARG, "workspace of %zu bytes < %zu required", workspace_bytes, pl.ws_bytes);
+  tattn::DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.seqlens = seqlens; a.o = o; a.lse = lse; a.workspace = workspace;
+  a.B = B; a.Nmax = Nmax; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.scale = softmax_scale; a.dtype = dtype;
+  return hip_status(tattn::launch_attn_decode(a, (hipStream_t)stream), "attn_decode_fp8kv launch");
+}
+
 }  // extern "C"

@@ -33,6 +33,33 @@ struct RotateArgs {
   int dtype;
 };
 
+// Decode step over an FP8 block-quantised KV cache.
+struct DecodeArgs {
+  const void* q;            // [B, Hq, d] 16-bit
+  const uint8_t* k;         // [B, Nmax, Hkv, d] E4M3 codes
+  const uint8_t* v;
+  const float* k_scale;     // [B, Hkv, ceil(Nmax/64)]
+  const float* v_scale;
+  const int* seqlens;       // [B] device
+  void* o;                  // [B, Hq, d] 16-bit
+  float* lse;               // [B, Hq] or NULL
+  void* workspace;          // plan_decode(...).ws_bytes bytes
+  int B, Nmax, Hq, Hkv, d;
+  float scale;
+  int dtype;
+};
+
+// Chunking of the cached sequence into workgroups, and the workspace it needs
+// (a function of the shapes only).
+struct DecodePlan {
+  int nhg;                  // groups of up to 16 query heads per KV head
+  int chunk;                // keys per workgroup (multiple of 256)
+  int nc;                   // chunks per sequence = ceil(Nmax / chunk)
+  long long ws_o_floats;    // partial outputs [B, Hq, nc, d]; then [B, Hq, nc, 2] (max, denominator)
+  size_t ws_bytes;
+};
+DecodePlan plan_decode(int B, int Nmax, int Hq, int Hkv);
+
 // Compute units of the current device (cached per device); persistent grids hold
 // one workgroup per CU.
 int device_cu_count();
@@ -41,5 +68,6 @@ int device_cu_count();
 hipError_t launch_attn_fwd16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_fp8(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_hadamard_rotate(const RotateArgs& a, hipStream_t stream);
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace tattn

@@ -13,8 +13,11 @@ FP8 workload first multiplies one seeded channel per head of Q and K by 20
 Decode workloads draw the query from tensor 0, each sequence's K and V cache
 rows from the streams [workload_id, 1, b] and [workload_id, 2, b], and the
 sequence lengths (a mix between Nmax/2 and Nmax, the last one full) from
-tensor 6; the cache is stored as E4M3 codes with 64-row block scales, made by
-the block quantiser from these values.
+tensor 6; the cache rows are rounded to the query's 16-bit type and stored as
+E4M3 codes with 64-row block scales, made by the block quantiser from these
+values.  ``random_e4m3_cache`` instead draws the codes themselves (every finite
+E4M3FN code equally likely) and the block scales, for edge cases that must
+cover all codes.
 
 The workloads follow the shapes the pages discuss: the tiny single-head check,
 multi-head fp16 (the B=2, N=2048, d=128 benchmark of the FA3 deep-dive page,
@@ -121,6 +124,17 @@ def decode_cache_f32(w: DecodeWorkload, b: int):
     k = np.random.default_rng([w.wid, 1, b]).standard_normal(size=(w.Nmax, w.Hkv, w.d), dtype=np.float32)
     v = np.random.default_rng([w.wid, 2, b]).standard_normal(size=(w.Nmax, w.Hkv, w.d), dtype=np.float32)
     return k, v
+
+
+def random_e4m3_cache(seed: int, B: int, N: int, H: int, d: int):
+    """Random finite E4M3FN codes (uint8 [B, N, H, d]; the two NaN codes 0x7f and
+    0xff are never drawn) and block scales (fp32 [B, H, ceil(N/64)], uniform in
+    [1/128, 1/32))."""
+    r = np.random.default_rng([2000 + seed, 7])
+    codes = r.integers(0, 254, size=(B, N, H, d), dtype=np.int64)
+    codes = codes + (codes >= 0x7F)              # skip 0x7f; 0xfe is the largest drawn, so 0xff never appears
+    scales = r.uniform(1 / 128, 1 / 32, size=(B, H, -(-N // 64))).astype(np.float32)
+    return codes.astype(np.uint8), scales
 
 
 def _rng(wid: int, tensor: int) -> np.random.Generator:
