@@ -1,7 +1,8 @@
 """Benchmark of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--causal 0|1]
-                    [--dtype bf16|fp16|fp8] [--no-cpu-baseline] [--no-fp8] [--copy-calibration]
+                    [--dtype bf16|fp16|fp8] [--no-cpu-baseline] [--no-fp8] [--no-decode]
+                    [--copy-calibration]
 
 A step is one attention forward over the workload's synthetic Q, K, V, already
 resident in HBM.  The default workload is one layer of a 70B-class model with
@@ -18,6 +19,11 @@ record under profiles/, the fp8 leg on the same shape (unless --no-fp8 or
 --dtype fp8) with its HBM-bound prologue timed with and without the fused
 rotary embedding, and the CPU oracle timed on a bounded row sample of the
 workload.
+
+The default run also times one decode step over an FP8 KV cache (B=4 sequences of up to
+131072 cached tokens, 64 query heads over 8 KV heads; "decode" in the JSON line, HBM roofline
+on algorithmic bytes); --workload decode_fp8kv_b4_h64kv8_n131072 makes the decode step the
+benchmarked step (GB/s, with the decode oracle timed on one sequence's KV head).
 
 --copy-calibration runs only a plain device copy of known size (for scaling
 the FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exits.
@@ -36,8 +42,10 @@ sys.path.insert(0, ROOT)
 
 # Dense matrix-core peaks of MI355X (TFLOP/s)
 PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp8": 5033.2}
+HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = {"attn_fwd16_kernel": ["attn_fwd16.hip", "tattn_pipeline.hpp", "tattn_device.hpp"],
-                  "attn_fwd_fp8_kernel": ["attn_fwd_fp8.hip", "tattn_pipeline.hpp", "tattn_device.hpp"]}
+                  "attn_fwd_fp8_kernel": ["attn_fwd_fp8.hip", "tattn_pipeline.hpp", "tattn_device.hpp"],
+                  "attn_decode_split_kernel": ["attn_decode.hip", "tattn_pipeline.hpp", "tattn_device.hpp"]}
 COPY_BYTES = 1 << 30
 
 
@@ -47,13 +55,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed launches first (the clocks take ~0.1 s of load to settle)")
-    ap.add_argument("--workload", default="gqa_bf16_h64kv8_n8192")
+    ap.add_argument("--workload", default="gqa_bf16_h64kv8_n8192",
+                    help="a prefill workload, or a decode workload (decode_fp8kv_...) to time the decode step alone")
     ap.add_argument("--causal", type=int, default=0)
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows per head in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg of the default run")
     return ap.parse_args()
 
 
@@ -168,6 +178,77 @@ def prologue_bytes(q, k, v):
     return 2 * n + n + 4 * blocks
 
 
+def decode_inputs(T, torch, W, w, dev):
+    """Query, E4M3 cache and device seqlens of a decode workload: seeded normal rows rounded to
+    the query's type, block-quantised on the GPU (timing input only)."""
+    q = W.to_torch(W.decode_query_f32(w), w.dtype).to(dev)
+    kc = torch.empty((w.B, w.Nmax, w.Hkv, w.d), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    nb = (w.Nmax + 63) // 64
+    ks = torch.empty((w.B, w.Hkv, nb), dtype=torch.float32, device=dev)
+    vs = torch.empty_like(ks)
+    for b in range(w.B):
+        kf, vf = W.decode_cache_f32(w, b)
+        T.hadamard_rotate(W.to_torch(kf[None], w.dtype).to(dev), None, quantize=True, out=kc[b:b + 1],
+                          scales=ks[b:b + 1])
+        T.hadamard_rotate(W.to_torch(vf[None], w.dtype).to(dev), None, quantize=True, out=vc[b:b + 1],
+                          scales=vs[b:b + 1])
+    seqlens = w.seqlens()
+    return q, kc, vc, ks, vs, torch.from_numpy(seqlens).to(dev), seqlens
+
+
+def decode_cpu_baseline(q, kc, ks, vc, vs, seqlens, w):
+    """The decode oracle on one (sequence, KV head) slice: the last (full-length) sequence, KV head 0."""
+    import numpy as np
+    from oracle import decode as D
+
+    b, g = w.B - 1, w.Hq // w.Hkv
+    qs = q[b:b + 1, :g].float().cpu().numpy()
+    kcs, vcs = kc[b:b + 1, :, :1].cpu().numpy(), vc[b:b + 1, :, :1].cpu().numpy()
+    kss, vss = ks[b:b + 1, :1].cpu().numpy(), vs[b:b + 1, :1].cpu().numpy()
+    L = int(seqlens[b])
+    t0 = time.perf_counter()
+    D.decode_attention(qs, kcs, kss, vcs, vss, [L])
+    dt = time.perf_counter() - t0
+    nbytes = L * w.d * 2 + 2 * 4 * ((L + 63) // 64) + 2 * g * w.d * 2
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"sequence {b} (L={L}), KV head 0 with its {g} query heads: {nbytes} algorithmic bytes "
+                      f"in {dt:.2f} s"}
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] + [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
+def decode_bench(T, torch, W, name, steps, warmup, stream, dev, cpu=True):
+    """Time one decode step (split + merge kernels) on a decode workload; HBM roofline."""
+    w = W.DECODE_WORKLOADS[name]
+    q, kc, vc, ks, vs, sl, seqlens = decode_inputs(T, torch, W, w, dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(T.decode_workspace_size(w.B, w.Nmax, w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
+    fn = lambda: T.attn_decode_fp8kv(q, kc, vc, ks, vs, sl, out=out, workspace=ws)
+    ms, wall = time_launches(torch, fn, steps, warmup, stream)
+    med, mn = launch_stats(torch, fn, steps, stream)
+    nbytes = w.hbm_bytes(seqlens)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": name, "B": w.B, "Nmax": w.Nmax, "seqlens": [int(x) for x in seqlens], "Hq": w.Hq,
+           "Hkv": w.Hkv, "d": w.d, "ms_per_step": round(ms, 4), "ms_median": med, "ms_min": mn,
+           "GB_per_s": round(gbps, 1), "tokens_per_s": round(w.B / (ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "traffic": recorded_traffic("attn_decode_split_kernel", name),
+                        "kernel": "attn_decode_split_kernel + attn_decode_merge_kernel (one step)",
+                        "bytes_per_launch": nbytes, "source_sha": source_hash("attn_decode_split_kernel")},
+           "wall_s_timed": round(wall, 3)}
+    if cpu:
+        res["cpu_baseline"] = decode_cpu_baseline(q, kc, ks, vc, vs, seqlens, w)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -188,6 +269,23 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return
+
+    if args.workload in W.DECODE_WORKLOADS:
+        print(f"[bench] decode {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+        d = decode_bench(T, torch, W, args.workload, args.steps, args.warmup, stream, dev,
+                         cpu=not args.no_cpu_baseline)
+        res = {"metric": "decode step HBM GB/s (algorithmic bytes: valid FP8 cache rows + scales + q + o)",
+               "value": d["GB_per_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+               "ms_per_step": d["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": "e4m3 cache / bf16", "data": "synthetic",
+               "config": {"workload": args.workload, "B": d["B"], "Nmax": d["Nmax"], "Hq": d["Hq"],
+                          "Hkv": d["Hkv"], "d": d["d"]},
+               "roofline": d["roofline"], "ms_median": d["ms_median"], "ms_min": d["ms_min"],
+               "tokens_per_s": d["tokens_per_s"], "wall_s_timed": d["wall_s_timed"]}
+        if "cpu_baseline" in d:
+            res["cpu_baseline"] = d["cpu_baseline"]
+        print(json.dumps(res), flush=True)
         return
 
     w = W.WORKLOADS[args.workload]
@@ -258,6 +356,9 @@ def main():
                       "frac_of_fp8_peak": round(flops / (fms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                       "prologue_ms": round(pms, 4), "speedup_vs_" + args.dtype: round(ms / fms, 3),
                       "speedup_incl_prologue": round(ms / (fms + pms), 3)}
+    if not args.no_decode:
+        res["decode"] = decode_bench(T, torch, W, "decode_fp8kv_b4_h64kv8_n131072", args.steps, args.warmup,
+                                     stream, dev, cpu=False)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, causal, args.cpu_rows, w.wid)
     print(json.dumps(res), flush=True)

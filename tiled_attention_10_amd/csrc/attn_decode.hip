@@ -29,9 +29,11 @@
 // m = max(m_a, m_b), z = z_a·2^(m_a−m) + z_b·2^(m_b−m) (the same for O), and the
 // workgroup writes one partial per query head to the caller's workspace.
 //
-// Merge kernel — one workgroup per (b, query head): folds the partials of the
-// chunks that hold keys (ceil(L_b / chunk) of them) with the same rule and
-// writes O = Σ/z in the query's type and the natural-log LSE.
+// Merge kernel — one workgroup per (b, query head): four groups of 128 threads
+// fold every fourth partial of the chunks that hold keys (ceil(L_b / chunk) of
+// them) with the same rule, eight loads in flight per thread, then the four
+// results are folded in LDS; it writes O = Σ/z in the query's type and the
+// natural-log LSE.
 #include "tattn_device.hpp"
 #include "tattn_pipeline.hpp"
 #include "tattn_launch.hpp"
@@ -49,9 +51,11 @@ constexpr int HALFB = KS * D;            // K (or V) bytes of one step: 4 KB
 constexpr int STEPB = 2 * HALFB;         // one ring stage
 constexpr int RINGB = STAGES * STEPB;    // 32 KB per wave
 constexpr int HG = 16;                   // query heads per workgroup
+constexpr int kOcc = 1;                  // workgroups per CU the registers are sized for
 constexpr float kSlack = 8.f;            // log2 units
-constexpr int kTargetItems = 4096;       // workgroups the chunk size aims for
-constexpr int kMinChunk = 256, kMaxChunk = 16384;
+constexpr int kTargetItems = 1024;       // workgroups the chunk size aims for
+constexpr int kMinChunk = 64 * NW;          // every wave starts on a scale block
+constexpr int kMaxChunk = 64 * 64 * NW;     // a wave spans at most 64 blocks (one per lane)
 
 // Physical 16-byte chunk of a 128-byte row = logical chunk ^ swz(row).  Both read
 // shapes then hit 16 distinct 16-byte bank windows: the score reads (16 rows
@@ -117,7 +121,7 @@ __device__ inline int seq_len(const DecParams& p, int b) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void attn_decode_split_kernel(DecParams p) {
+__global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[NW * RINGB];
   lds_char* const lds = (lds_char*)smem;
 
@@ -322,25 +326,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_split_kernel(DecParam
   }
 }
 
+constexpr int kMergeGroups = 4;          // chunk partials folded in parallel per (b, head)
+constexpr int kMergeBatch = 8;           // partials loaded before they are folded
+
 template <typename T>
-__global__ __launch_bounds__(D) void attn_decode_merge_kernel(DecParams p) {
-  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(D * kMergeGroups) void attn_decode_merge_kernel(DecParams p) {
+  __shared__ float red[kMergeGroups][D + 2];
+  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x % D, grp = threadIdx.x / D;
   const int L = seq_len(p, b);
   const int ncb = (L + p.chunk - 1) / p.chunk;
   const long long row0 = ((long long)b * p.Hq + hq) * p.nc;
+  // Group grp folds partials grp, grp + G, grp + 2G, ...; the loads of a batch are
+  // all issued before the first is used.
   float M = -INFINITY, Z = 0.f, O = 0.f;
-  for (int i = 0; i < ncb; ++i) {
-    const float mi = p.ws_ml[2 * (row0 + i)], zi = p.ws_ml[2 * (row0 + i) + 1];
-    const float oi = p.ws_o[(row0 + i) * D + c];
-    const float Mn = __builtin_fmaxf(M, mi);
-    const float a = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
-    const float f = mi == -INFINITY ? 0.f : fast_exp2(mi - Mn);
-    O = O * a + oi * f;
-    Z = Z * a + zi * f;
-    M = Mn;
+  for (int i0 = grp; i0 < ncb; i0 += kMergeGroups * kMergeBatch) {
+    float mi[kMergeBatch], zi[kMergeBatch], oi[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int i = min(i0 + u * kMergeGroups, ncb - 1);
+      mi[u] = p.ws_ml[2 * (row0 + i)];
+      zi[u] = p.ws_ml[2 * (row0 + i) + 1];
+      oi[u] = p.ws_o[(row0 + i) * D + c];
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (i0 + u * kMergeGroups >= ncb) break;
+      const float Mn = __builtin_fmaxf(M, mi[u]);
+      const float a = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+      const float f = mi[u] == -INFINITY ? 0.f : fast_exp2(mi[u] - Mn);
+      O = O * a + oi[u] * f;
+      Z = Z * a + zi[u] * f;
+      M = Mn;
+    }
   }
-  p.o[((long long)b * p.Hq + hq) * D + c] = T::from_f32(Z > 0.f ? O / Z : 0.f);
-  if (c == 0 && p.lse != nullptr) p.lse[(long long)b * p.Hq + hq] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : -INFINITY;
+  red[grp][c] = O;
+  if (c == 0) {
+    red[grp][D] = M;
+    red[grp][D + 1] = Z;
+  }
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < kMergeGroups; ++g) Mt = __builtin_fmaxf(Mt, red[g][D]);
+  float Ot = 0.f, Zt = 0.f;
+#pragma unroll
+  for (int g = 0; g < kMergeGroups; ++g) {
+    const float f = red[g][D] == -INFINITY ? 0.f : fast_exp2(red[g][D] - Mt);
+    Ot = fmaf(red[g][c], f, Ot);
+    Zt = fmaf(red[g][D + 1], f, Zt);
+  }
+  p.o[((long long)b * p.Hq + hq) * D + c] = T::from_f32(Zt > 0.f ? Ot / Zt : 0.f);
+  if (c == 0 && p.lse != nullptr) p.lse[(long long)b * p.Hq + hq] = Zt > 0.f ? (Mt + __log2f(Zt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -388,7 +425,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                      dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_merge_kernel<T>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(D), 0, stream, p);
+  hipLaunchKernelGGL((attn_decode_merge_kernel<T>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(D * kMergeGroups), 0,
+                     stream, p);
   return hipGetLastError();
 }
 }  // namespace
