@@ -283,7 +283,10 @@ __global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecPa
   z += __shfl_xor(z, 16, 64);
   z += __shfl_xor(z, 32, 64);
 
-  // Merge the four waves' partials in LDS (each wave writes into its own ring).
+  // Merge the four waves' partials in LDS (each wave writes into its own ring).  O is
+  // kept as 16-byte units [channel block cb][lane group lq][head] (channels 16cb + 4lq
+  // .. +3 of a head per unit), so that the 16 lanes of a store, and of a load below,
+  // touch 16 distinct bank windows.
   float* mine = (float*)(smem + wave * RINGB);
   if (lq == 0) {
     mine[li] = m_ref;
@@ -292,11 +295,13 @@ __global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecPa
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) {
     f32x4_t w = oacc[cb] * vsmax;
-    *(f32x4_t*)(mine + 2 * HG + li * D + 16 * cb + 4 * lq) = w;
+    *(f32x4_t*)(mine + 2 * HG + 4 * ((4 * cb + lq) * HG + li)) = w;
   }
   __syncthreads();
   {
-    const int h = tid >> 4, ch = 8 * (tid & 15);
+    // thread: head h, channels 8k .. 8k + 7 (units (cb, lq) = (k/2, 2(k%2)) and (k/2, 2(k%2) + 1))
+    const int h = tid & 15, k = tid >> 4, ch = 8 * k;
+    const int u0 = (4 * (k >> 1) + 2 * (k & 1)) * HG + h;
     float mw[NW], M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -310,15 +315,15 @@ __global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecPa
       const float* src = (const float*)(smem + w * RINGB);
       const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
       zt = fmaf(src[HG + h], f, zt);
-      o0 += *(const f32x4_t*)(src + 2 * HG + h * D + ch) * f;
-      o1 += *(const f32x4_t*)(src + 2 * HG + h * D + ch + 4) * f;
+      o0 += *(const f32x4_t*)(src + 2 * HG + 4 * u0) * f;
+      o1 += *(const f32x4_t*)(src + 2 * HG + 4 * (u0 + HG)) * f;
     }
     const int hh = hg * HG + h;
     if (hh < p.group) {
       const long long row = ((long long)b * p.Hq + kvh * p.group + hh) * p.nc + ci;
       *(f32x4_t*)(p.ws_o + row * D + ch) = o0;
       *(f32x4_t*)(p.ws_o + row * D + ch + 4) = o1;
-      if ((tid & 15) == 0) {
+      if (k == 0) {
         p.ws_ml[2 * row] = M;
         p.ws_ml[2 * row + 1] = zt;
       }
