@@ -20,7 +20,9 @@ record under profiles/, the fp8 leg on the same shape (unless --no-fp8 or
 rotary embedding, and the CPU oracle timed on a bounded row sample of the
 workload.
 
-The default run also times one decode step over an FP8 KV cache (B=4 sequences of up to
+The default run also reports the fp8 path's output RMSE against exact attention of the 16-bit
+inputs, with and without the Hadamard rotation, on the outlier workload ("fp8_rmse"), and times
+one decode step over an FP8 KV cache (B=4 sequences of up to
 131072 cached tokens, 64 query heads over 8 KV heads; "decode" in the JSON line, HBM roofline
 on algorithmic bytes); --workload decode_fp8kv_b4_h64kv8_n131072 makes the decode step the
 benchmarked step (GB/s, with the decode oracle timed on one sequence's KV head).
@@ -176,6 +178,39 @@ def prologue_bytes(q, k, v):
     n = q.numel() + k.numel() + v.numel()
     blocks = sum(t.shape[0] * t.shape[2] * ((t.shape[1] + 63) // 64) for t in (q, k, v))
     return 2 * n + n + 4 * blocks
+
+
+def fp8_rmse_leg(T, torch, W, dev, nrows=256):
+    """Output RMSE of the fp8 path against exact attention of the unquantised 16-bit inputs,
+    with and without the random-sign Hadamard rotation of Q and K, on the outlier workload
+    (one x20 channel per head).  The reference is plain PyTorch in fp32 on the GPU, on
+    ``nrows`` seeded query rows per (batch, head)."""
+    import numpy as np
+
+    w = W.WORKLOADS["fp8_outlier_b2_h16_n4096"]
+    q, k, v = (W.to_torch(x, "bf16").to(dev) for x in W.qkv_f32(w))
+    rows = torch.from_numpy(np.sort(np.random.default_rng(w.wid).choice(w.N, nrows, replace=False))).to(dev)
+    g = w.Hq // w.Hkv
+    qf, kf, vf = q.float(), k.float(), v.float()
+    ref = torch.empty((w.B, nrows, w.Hq, w.d), dtype=torch.float32, device=dev)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            qs = qf[b, rows, h, :].contiguous()
+            kt = kf[b, :, h // g, :].t().contiguous()
+            s = (qs @ kt) * w.scale
+            ref[b, :, h, :] = torch.softmax(s, dim=-1) @ vf[b, :, h // g, :].contiguous()
+    signs = torch.from_numpy(W.rotation_signs(w.wid, w.d)).to(dev)
+    res = {}
+    for rot in (False, True):
+        sg = signs if rot else None
+        q8, sq = T.hadamard_rotate(q, sg, quantize=True)
+        k8, sk = T.hadamard_rotate(k, sg, quantize=True)
+        v8, sv = T.hadamard_rotate(v, None, quantize=True)
+        o = T.attn_fwd_fp8(q8, k8, v8, sq, sk, sv)[:, rows].float()
+        res["with_hadamard" if rot else "without_hadamard"] = round(((o - ref) ** 2).mean().sqrt().item(), 6)
+    res["ratio_without_over_with"] = round(res["without_hadamard"] / res["with_hadamard"], 3)
+    res["sample"] = f"{w.name}: {nrows} seeded query rows x {w.Hq} heads x B={w.B}; fp32 torch reference on the GPU"
+    return res
 
 
 def decode_inputs(T, torch, W, w, dev):
@@ -356,6 +391,8 @@ def main():
                       "frac_of_fp8_peak": round(flops / (fms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                       "prologue_ms": round(pms, 4), "speedup_vs_" + args.dtype: round(ms / fms, 3),
                       "speedup_incl_prologue": round(ms / (fms + pms), 3)}
+    if args.dtype != "fp8" and not args.no_fp8:
+        res["fp8_rmse"] = fp8_rmse_leg(T, torch, W, dev)
     if not args.no_decode:
         res["decode"] = decode_bench(T, torch, W, "decode_fp8kv_b4_h64kv8_n131072", args.steps, args.warmup,
                                      stream, dev, cpu=False)
