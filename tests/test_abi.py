@@ -80,7 +80,7 @@ def fp8(L, d=128, out_dtype=2, scales=P, causal=0, q8=P, N=128):
 @pytest.mark.parametrize("kw,status", [
     (dict(d=64), UNSUPPORTED), (dict(out_dtype=7), UNSUPPORTED), (dict(scales=None), INVALID),
     (dict(causal=-1), INVALID), (dict(q8=BAD), MISALIGNED), (dict(scales=P + 1), MISALIGNED),
-    (dict(q8=None), INVALID), (dict(N=-5), INVALID),
+    (dict(q8=None), INVALID), (dict(N=-5), INVALID), (dict(N=262145), UNSUPPORTED),
 ])
 def test_attn_fwd_fp8_rejects(L, kw, status):
     assert fp8(L, **kw) == status
@@ -124,7 +124,8 @@ def decode(L, q=P, kc=P, vc=P, ks=P, vs=P, sl=P, o=P, lse=None, ws=P, wsb=1 << 3
     (dict(scale=0.0), INVALID), (dict(scale=float("inf")), INVALID), (dict(q=BAD), MISALIGNED),
     (dict(vc=P + 4), MISALIGNED), (dict(ws=P + 8), MISALIGNED), (dict(ks=P + 2), MISALIGNED),
     (dict(sl=P + 1), MISALIGNED), (dict(lse=P + 3), MISALIGNED), (dict(wsb=16), INVALID),
-    (dict(B=1 << 20, Nmax=1 << 20, Hq=64, Hkv=8), INVALID),
+    (dict(B=1 << 20, Nmax=1 << 20, Hq=64, Hkv=8), INVALID), (dict(B=65536, Nmax=8), INVALID),
+    (dict(Hq=65537 * 2, Hkv=65537, Nmax=8), INVALID), (dict(Hq=4, Hkv=4, d=0), UNSUPPORTED),
 ])
 def test_attn_decode_fp8kv_rejects(L, kw, status):
     assert decode(L, **kw) == status
