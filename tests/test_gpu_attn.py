@@ -120,6 +120,21 @@ def test_large_workloads_sampled_rows(name, causal):
     assert np.isfinite(o).all()
 
 
+@pytest.mark.parametrize("causal,N", [(False, 2048), (True, 4096)])
+def test_uneven_persistent_shares(causal, N):
+    # 320 work items on a 256-workgroup grid with the XCD-contiguous dealing on: some
+    # workgroups walk two items, the others one; every row of every 4th head is checked
+    # at item boundaries and at random.
+    q, k, v = (W.to_torch(x, "bf16") for x in W.random_qkv(41, 1, N, 40, 8, 128))
+    o = run(q, k, v, causal)
+    rows = sample_rows(N, 41, n=96, bm=256)
+    heads = list(range(0, 40, 4)) + [39]
+    ref, _ = A.attention_rows(q, k, v, rows, None, causal, heads=heads)
+    err = np.abs(o[:, rows][:, :, heads] - ref).max()
+    print(f"uneven shares causal={causal}: max|dO| = {err:.3e}")
+    assert err <= TOL["bf16"] and np.isfinite(o).all()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_causal_row0_is_v0_bit_exact(dtype):
     q, k, v = (W.to_torch(x, dtype) for x in W.random_qkv(31, 2, 300, 4, 2, 128))

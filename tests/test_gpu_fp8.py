@@ -71,6 +71,21 @@ def test_fp8_small_shapes_against_emulation(shape, causal):
     assert np.abs(lse - exact_lse).max() <= 0.5
 
 
+def test_fp8_uneven_persistent_shares():
+    # 320 work items on a 256-workgroup grid (XCD-contiguous dealing on): some workgroups
+    # walk two items, the others one.
+    q, k, v = (W.to_torch(x, "bf16") for x in W.random_qkv(42, 1, 2048, 40, 8, 128))
+    q8, k8, v8, sq, sk, sv = quantise_all(q, k, v, None)
+    o = run_fp8(q8, k8, v8, sq, sk, sv, False)
+    rows = np.unique(np.concatenate([[0, 255, 256, 2047], np.random.default_rng(42).integers(0, 2048, 64)]))
+    exact, _ = A.attention_rows(q, k, v, rows)
+    emul = fp8_attention_emul(q8, k8, v8, sq, sk, sv, None, False, rows=rows)
+    e_gpu, e_emul = rmse(o[:, rows], exact), rmse(emul, exact)
+    print(f"uneven shares: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
+    assert np.isfinite(o).all()
+    assert e_gpu <= 1.5 * e_emul + 1e-3
+
+
 def test_fp8_causal_row0_is_dequantised_v0():
     # Row 0 sees only key 0: O = V8[0]·sv0 · (e4m3(p̃)/p̃), one rounded probability, so the
     # output is proportional to the dequantised V row with a factor within E4M3's 2^-4.
