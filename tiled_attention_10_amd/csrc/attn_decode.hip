@@ -29,11 +29,13 @@
 // m = max(m_a, m_b), z = z_a·2^(m_a−m) + z_b·2^(m_b−m) (the same for O), and the
 // workgroup writes one partial per query head to the caller's workspace.
 //
-// Merge kernel — one workgroup per (b, query head): four groups of 128 threads
-// fold every fourth partial of the chunks that hold keys (ceil(L_b / chunk) of
-// them) with the same rule, eight loads in flight per thread, then the four
-// results are folded in LDS; it writes O = Σ/z in the query's type and the
-// natural-log LSE.
+// Merge kernel — one workgroup per (b, query head): G groups of 128 threads (G = 8
+// when there are few (b, head) merges, else 4) fold every G-th partial of the
+// chunks that hold keys (ceil(L_b / chunk) of them) with the same rule, eight
+// loads in flight per thread, then the G results are folded in LDS; it writes
+// O = Σ/z in the query's type and the natural-log LSE.
+#include <algorithm>
+
 #include "tattn_device.hpp"
 #include "tattn_pipeline.hpp"
 #include "tattn_launch.hpp"
@@ -54,6 +56,8 @@ constexpr int HG = 16;                   // query heads per workgroup
 constexpr int kOcc = 1;                  // workgroups per CU the registers are sized for
 constexpr float kSlack = 8.f;            // log2 units
 constexpr int kTargetItems = 1024;       // workgroups the chunk size aims for
+constexpr int kMinItems = 256;           // ... but it is raised toward kLongChunk keys while
+constexpr int kLongChunk = 4096;         // at least this many workgroups remain
 constexpr int kMinChunk = 64 * NW;          // every wave starts on a scale block
 constexpr int kMaxChunk = 64 * 64 * NW;     // a wave spans at most 64 blocks (one per lane)
 
@@ -331,10 +335,11 @@ __global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecPa
   }
 }
 
-constexpr int kMergeGroups = 4;          // chunk partials folded in parallel per (b, head)
 constexpr int kMergeBatch = 8;           // partials loaded before they are folded
+constexpr int kWideMergeBelow = 256;     // fewer (b, head) merges than this: 8 groups each, else 4
 
-template <typename T>
+// kMergeGroups groups of D threads fold chunk partials in parallel per (b, head).
+template <typename T, int kMergeGroups>
 __global__ __launch_bounds__(D * kMergeGroups) void attn_decode_merge_kernel(DecParams p) {
   __shared__ float red[kMergeGroups][D + 2];
   const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x % D, grp = threadIdx.x / D;
@@ -392,7 +397,12 @@ DecodePlan plan_decode(int B, int Nmax, int Hq, int Hkv) {
   const int group = Hq / Hkv;
   pl.nhg = (group + HG - 1) / HG;
   const long long pairs = (long long)B * Hkv * pl.nhg;
-  long long chunk = (pairs * Nmax + kTargetItems - 1) / kTargetItems;
+  // Aim for kTargetItems workgroups; when that makes chunks shorter than kLongChunk keys
+  // (a few long sequences), lengthen them toward kLongChunk as long as kMinItems
+  // workgroups remain: short workgroups spend much of their time filling the ring.
+  const long long work = pairs * Nmax;
+  long long chunk = (work + kTargetItems - 1) / kTargetItems;
+  if (chunk < kLongChunk) chunk = std::max(chunk, std::min<long long>(kLongChunk, (work + kMinItems - 1) / kMinItems));
   chunk = (chunk + kMinChunk - 1) / kMinChunk * kMinChunk;
   chunk = chunk < kMinChunk ? kMinChunk : (chunk > kMaxChunk ? kMaxChunk : chunk);
   pl.chunk = (int)chunk;
@@ -430,8 +440,10 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                      dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_decode_merge_kernel<T>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(D * kMergeGroups), 0,
-                     stream, p);
+  if ((long long)a.Hq * a.B < kWideMergeBelow)
+    hipLaunchKernelGGL((attn_decode_merge_kernel<T, 8>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(D * 8), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_merge_kernel<T, 4>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(D * 4), 0, stream, p);
   return hipGetLastError();
 }
 }  // namespace
