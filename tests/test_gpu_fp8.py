@@ -86,6 +86,38 @@ def test_fp8_uneven_persistent_shares():
     assert e_gpu <= 1.5 * e_emul + 1e-3
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_full_gqa_layer_sampled_rows(causal):
+    # The benchmark's fp8 configuration: the 64/8-head 8k layer, Q and K rotated with the
+    # seeded signs and quantised (V quantised) by the GPU quantiser.  The oracle quantises
+    # one query head per KV group and all of K and V itself; the codes must agree bit for
+    # bit, and sampled rows are held to the emulation bound.
+    w = W.WORKLOADS["gqa_bf16_h64kv8_n8192"]
+    q, k, v = (W.to_torch(x, "bf16") for x in W.qkv_f32(w))
+    s = W.rotation_signs(w.wid, w.d)
+    sg = torch.from_numpy(s).to(DEV)
+    q8, sq = T.hadamard_rotate(q.to(DEV), sg, quantize=True)
+    k8, sk = T.hadamard_rotate(k.to(DEV), sg, quantize=True)
+    v8, sv = T.hadamard_rotate(v.to(DEV), None, quantize=True)
+    print(f"[attn_fwd_fp8] full GQA layer causal={causal}", flush=True)
+    o = T.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal).float().cpu().numpy()
+    heads = list(range(0, w.Hq, w.Hq // w.Hkv))                     # one per KV head
+    qo8, sqo = quant.quantize(q[:, :, heads].float().numpy(), s)
+    ko8, sko = quant.quantize(k.float().numpy(), s)
+    vo8, svo = quant.quantize(v.float().numpy(), None)
+    assert np.array_equal(q8[:, :, heads].cpu().numpy(), qo8) and np.array_equal(sq[:, heads].cpu().numpy(), sqo)
+    assert np.array_equal(k8.cpu().numpy(), ko8) and np.array_equal(sv.cpu().numpy(), svo)
+    rows = np.unique(np.concatenate([[0, 63, 64, 255, 256, w.N - 1], np.random.default_rng(7).integers(0, w.N, 48)]))
+    emul = fp8_attention_emul(qo8, ko8, vo8, sqo, sko, svo, None, causal, rows=rows)
+    exact, _ = A.attention_rows(q[:, :, heads].contiguous(), k, v, rows, None, causal)
+    got = o[:, rows][:, :, heads]
+    e_gpu, e_emul = rmse(got, exact), rmse(emul, exact)
+    print(f"full layer causal={causal}: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
+    assert np.isfinite(o).all()
+    assert e_gpu <= 1.5 * e_emul + 1e-3
+    assert e_gpu < 0.1 * np.std(exact)
+
+
 def test_fp8_causal_row0_is_dequantised_v0():
     # Row 0 sees only key 0: O = V8[0]·sv0 · (e4m3(p̃)/p̃), one rounded probability, so the
     # output is proportional to the dequantised V row with a factor within E4M3's 2^-4.
