@@ -120,6 +120,21 @@ def test_large_workloads_sampled_rows(name, causal):
     assert np.isfinite(o).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_long_sequence_d64(dtype):
+    # d = 64 at 64k keys, causal, GQA 4/2: sampled rows at tile and item boundaries.
+    N = 65536
+    q, k, v = (W.to_torch(x, dtype) for x in W.random_qkv(44, 1, N, 4, 2, 64))
+    o, lse = run(q, k, v, True, lse=True)
+    rows = sample_rows(N, 44, n=64, bm=256)
+    ref, ref_lse = A.attention_rows(q, k, v, rows, None, True)
+    err = np.abs(o[:, rows] - ref).max()
+    print(f"d=64 N={N} {dtype}: max|dO| = {err:.3e}")
+    assert err <= TOL[dtype] and np.isfinite(o).all()
+    tol = lse_tol(q, k, dtype, rows=rows)
+    assert (np.abs(lse[:, :, rows] - ref_lse) <= tol + 1e-6 * np.abs(ref_lse)).all()
+
+
 @pytest.mark.parametrize("causal,N", [(False, 2048), (True, 4096)])
 def test_uneven_persistent_shares(causal, N):
     # 320 work items on a 256-workgroup grid with the XCD-contiguous dealing on: some

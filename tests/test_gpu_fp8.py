@@ -118,6 +118,23 @@ def test_fp8_full_gqa_layer_sampled_rows(causal):
     assert e_gpu < 0.1 * np.std(exact)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_maximum_sequence(causal):
+    # N = 262144, the path's limit: the per-head tables of K and V block scales in LDS
+    # (4096 blocks) are full.
+    N = 262144
+    q, k, v = (W.to_torch(x, "bf16") for x in W.random_qkv(43, 1, N, 2, 1, 128))
+    q8, k8, v8, sq, sk, sv = quantise_all(q, k, v, None)
+    o = run_fp8(q8, k8, v8, sq, sk, sv, causal)
+    rows = np.array([0, 1, 63, 64, 4095, 65536, N // 2 + 17, N - 65, N - 64, N - 1])
+    exact, _ = A.attention_rows(q, k, v, rows, None, causal)
+    emul = fp8_attention_emul(q8, k8, v8, sq, sk, sv, None, causal, rows=rows)
+    e_gpu, e_emul = rmse(o[:, rows], exact), rmse(emul, exact)
+    print(f"N={N} causal={causal}: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
+    assert np.isfinite(o).all()
+    assert e_gpu <= 1.5 * e_emul + 1e-3
+
+
 def test_fp8_causal_row0_is_dequantised_v0():
     # Row 0 sees only key 0: O = V8[0]·sv0 · (e4m3(p̃)/p̃), one rounded probability, so the
     # output is proportional to the dequantised V row with a factor within E4M3's 2^-4.
