@@ -136,6 +136,25 @@ def test_decode_fp16_softmax_scale():
     case(32, 3, 900, 8, 2, [900, 1, 450], "fp16", scale=0.3)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_decode_single_chunk_plan(dtype):
+    # Nmax fits in one chunk: the split kernel writes O and LSE itself and no merge runs;
+    # empty sequences still get O = 0 and LSE = -inf.
+    B, N, Hq, Hkv = 5, 250, 16, 2
+    assert T.decode_workspace_size(B, N, Hq, Hkv, 128) == B * Hq * 1 * 130 * 4
+    q, k, v = W.random_qkv(36, B, 1, Hq, Hkv, 128, Nk=N)
+    q16, k16, v16 = W.to_torch(q[:, 0], dtype), W.to_torch(k, dtype), W.to_torch(v, dtype)
+    kc, ks = quant.quantize(k16.float().numpy())
+    vc, vs = quant.quantize(v16.float().numpy())
+    seqlens = [250, 1, 0, 129, 64]
+    o, lse = run_gpu(q16, kc, ks, vc, vs, seqlens)
+    assert np.array_equal(o[2], np.zeros_like(o[2])) and np.all(lse[2] == -np.inf)
+    live = [0, 1, 3, 4]
+    ref, ref_lse = D.decode_attention(q16.float().numpy()[live], kc[live], ks[live], vc[live], vs[live],
+                                      [seqlens[i] for i in live], return_lse=True)
+    check(o[live], lse[live], ref, ref_lse, vmax_per_head(vc[live], vs[live], [seqlens[i] for i in live], Hq), dtype)
+
+
 def test_decode_every_code():
     B, N, Hq, Hkv = 2, 2048, 8, 2
     kc, ks = W.random_e4m3_cache(1, B, N, Hkv, 128)

@@ -27,7 +27,8 @@
 //
 // The waves' partial results (m, z, O) are merged in LDS with the rule
 // m = max(m_a, m_b), z = z_a·2^(m_a−m) + z_b·2^(m_b−m) (the same for O), and the
-// workgroup writes one partial per query head to the caller's workspace.
+// workgroup writes one partial per query head to the caller's workspace — or,
+// when one chunk covers Nmax, the final O and LSE, and the merge is not launched.
 //
 // Merge kernel — one workgroup per (b, query head): G groups of 128 threads (G = 8
 // when there are few (b, head) merges, else 4) fold every G-th partial of the
@@ -135,7 +136,17 @@ __global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecPa
   const int kvh = blockIdx.y / p.nhg, hg = blockIdx.y % p.nhg;
   const int L = seq_len(p, b);
   const int c0 = ci * p.chunk;
-  if (c0 >= L) return;                           // no keys in this chunk (uniform)
+  if (c0 >= L) {                                 // no keys in this chunk (uniform)
+    if (p.nc == 1) {                             // single-chunk plan: an empty sequence's output here
+      const int h = threadIdx.x & 15, ch = 8 * (threadIdx.x >> 4), hh = hg * HG + h;
+      if (hh < p.group) {
+        const long long bh = (long long)b * p.Hq + kvh * p.group + hh;
+        *(u32x4*)(p.o + bh * D + ch) = u32x4{0u, 0u, 0u, 0u};
+        if (ch == 0 && p.lse != nullptr) p.lse[bh] = -INFINITY;
+      }
+    }
+    return;
+  }
 
   const int wlen = p.chunk / NW;
   const int kbeg = c0 + wave * wlen;
@@ -324,12 +335,25 @@ __global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecPa
     }
     const int hh = hg * HG + h;
     if (hh < p.group) {
-      const long long row = ((long long)b * p.Hq + kvh * p.group + hh) * p.nc + ci;
-      *(f32x4_t*)(p.ws_o + row * D + ch) = o0;
-      *(f32x4_t*)(p.ws_o + row * D + ch + 4) = o1;
-      if (k == 0) {
-        p.ws_ml[2 * row] = M;
-        p.ws_ml[2 * row + 1] = zt;
+      const long long bh = (long long)b * p.Hq + kvh * p.group + hh;
+      if (p.nc == 1) {
+        // The chunk is the whole sequence: this is the final result and no merge runs.
+        const float den = zt > 0.f ? zt : 1.f;
+        u32x4 w;
+        w[0] = T::pack(o0[0] / den, o0[1] / den);
+        w[1] = T::pack(o0[2] / den, o0[3] / den);
+        w[2] = T::pack(o1[0] / den, o1[1] / den);
+        w[3] = T::pack(o1[2] / den, o1[3] / den);
+        *(u32x4*)(p.o + bh * D + ch) = w;
+        if (k == 0 && p.lse != nullptr) p.lse[bh] = zt > 0.f ? (M + __log2f(zt)) * kLn2 : -INFINITY;
+      } else {
+        const long long row = bh * p.nc + ci;
+        *(f32x4_t*)(p.ws_o + row * D + ch) = o0;
+        *(f32x4_t*)(p.ws_o + row * D + ch + 4) = o1;
+        if (k == 0) {
+          p.ws_ml[2 * row] = M;
+          p.ws_ml[2 * row + 1] = zt;
+        }
       }
     }
   }
@@ -439,7 +463,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_decode_split_kernel<T>), dim3((unsigned)pl.nc, (unsigned)(a.Hkv * pl.nhg), (unsigned)a.B),
                      dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || pl.nc == 1) return e;   // one chunk per sequence: the split kernel wrote O
   if ((long long)a.Hq * a.B < kWideMergeBelow)
     hipLaunchKernelGGL((attn_decode_merge_kernel<T, 8>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(D * 8), 0, stream, p);
   else
