@@ -121,9 +121,11 @@ def test_decode_ragged_lengths():
     case(11, 8, 700, 4, 4, [1, 2, 31, 33, 64, 65, 257, 700], "bf16")
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (24, 1), (5, 1), (32, 2), (3, 3)])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (24, 1), (5, 1), (32, 2), (3, 3), (48, 1), (64, 1), (80, 1), (128, 2)])
 def test_decode_group_sizes(Hq, Hkv):
-    # 16 query heads fill one product; 24 needs two head groups, the second partly empty
+    # 16 query heads fill one product; 24 needs two head groups, the second partly empty.
+    # Up to four groups share one workgroup's K/V reads (48: three, 64: four); 80 query
+    # heads per KV head take a second workgroup for the fifth group.
     case(20 + Hq, 2, 600, Hq, Hkv, [600, 377], "bf16")
 
 
