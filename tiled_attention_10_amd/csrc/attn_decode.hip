@@ -7,9 +7,10 @@
 // Split kernel — one workgroup per (sequence b, KV head, group of up to 16 of
 // its query heads, chunk of the sequence).  The 4 waves take consecutive
 // quarters of the chunk and run independently: each streams its keys 32 at a
-// time through a private 4-stage LDS ring filled by LDS-DMA (K and V rows of
-// one step, 8 KB), so no barrier is needed inside the loop and up to three
-// steps per wave are in flight.  Per step, on 16x16x32 matrix-core products
+// time through a private LDS ring filled by LDS-DMA (K and V rows of one step,
+// 8 KB), so no barrier is needed inside the loop.  Long chunks use 4 stages (up
+// to three steps per wave in flight) and one workgroup per CU; few or short
+// workgroups use 2 stages and two workgroups per CU.  Per step, on 16x16x32 matrix-core products
 // with the query heads as the N dimension:
 //
 //   Sᵀ = K·Qᵀ      A = 16 key rows x 32 channels (E4M3 codes converted exactly to
@@ -49,12 +50,9 @@ constexpr int D = 128;
 constexpr int NW = 4;                    // waves per workgroup
 constexpr int kThreads = 64 * NW;
 constexpr int KS = 32;                   // keys per step
-constexpr int STAGES = 4;
 constexpr int HALFB = KS * D;            // K (or V) bytes of one step: 4 KB
 constexpr int STEPB = 2 * HALFB;         // one ring stage
-constexpr int RINGB = STAGES * STEPB;    // 32 KB per wave
 constexpr int HG = 16;                   // query heads per workgroup
-constexpr int kOcc = 1;                  // workgroups per CU the registers are sized for
 constexpr float kSlack = 8.f;            // log2 units
 constexpr int kTargetItems = 1024;       // workgroups the chunk size aims for
 constexpr int kMinItems = 256;           // ... but it is raised toward kLongChunk keys while
@@ -125,8 +123,13 @@ __device__ inline int seq_len(const DecParams& p, int b) {
   return min(max(p.seqlens[b], 0), p.Nmax);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, kOcc) void attn_decode_split_kernel(DecParams p) {
+// STAGES ring stages per wave (RINGB bytes), OCC workgroups per CU: 4 stages and one
+// workgroup per CU stream long chunks best; 2 stages and two workgroups per CU let one
+// workgroup's pipeline fill overlap another's streaming when workgroups are few or short.
+template <typename T, int STAGES, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void attn_decode_split_kernel(DecParams p) {
+  constexpr int RINGB = STAGES * STEPB;
+  static_assert(RINGB >= 4 * (2 * HG + HG * D) + 256, "the ring holds a wave's merge block");
   __shared__ __attribute__((aligned(1024))) char smem[NW * RINGB];
   lds_char* const lds = (lds_char*)smem;
 
@@ -460,8 +463,12 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   p.nc = pl.nc;
   p.chunk = pl.chunk;
   p.c = (float)((double)a.scale * 1.4426950408889634);
-  hipLaunchKernelGGL((attn_decode_split_kernel<T>), dim3((unsigned)pl.nc, (unsigned)(a.Hkv * pl.nhg), (unsigned)a.B),
-                     dim3(kThreads), 0, stream, p);
+  const dim3 grid((unsigned)pl.nc, (unsigned)(a.Hkv * pl.nhg), (unsigned)a.B);
+  const long long wgs = (long long)pl.nc * a.Hkv * pl.nhg * a.B;
+  if (pl.nc <= 2 || wgs <= 2LL * device_cu_count())   // short sequences, or few workgroups
+    hipLaunchKernelGGL((attn_decode_split_kernel<T, 2, 2>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_split_kernel<T, 4, 1>), grid, dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nc == 1) return e;   // one chunk per sequence: the split kernel wrote O
   if ((long long)a.Hq * a.B < kWideMergeBelow)
