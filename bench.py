@@ -13,7 +13,8 @@ hadamard_rotate (rotation + quantisation, timed separately as the prologue).
 
 Prints ONE JSON line: throughput in TFLOPS (4·N²·d·Hq·B per step, halved when
 causal; mean over the timed steps, plus per-launch median and min), the
-attention kernel's roofline against the dense matrix-core peak,
+attention kernel's roofline against the dense matrix-core peak (and against that peak
+scaled to the shader clock a one-wave probe on a second stream measures under the same load),
 its HBM traffic when a counter measurement of the current kernel source is on
 record under profiles/, the fp8 leg on the same shape (unless --no-fp8 or
 --dtype fp8) with its HBM-bound prologue timed with and without the fused
@@ -178,6 +179,32 @@ def prologue_bytes(q, k, v):
     n = q.numel() + k.numel() + v.numel()
     blocks = sum(t.shape[0] * t.shape[2] * ((t.shape[1] + 63) // 64) for t in (q, k, v))
     return 2 * n + n + 4 * blocks
+
+
+def measured_clock_ghz(torch, fn, dev, launches=20):
+    """Shader clock (GHz) while the benchmarked kernel runs: a one-wave probe on a second
+    stream (default priority) reads the shader cycle counter against the 100 MHz
+    reference counter for ~20 ms while ``launches`` kernels run on the current stream.
+    None if the probe library is missing."""
+    import ctypes
+
+    path = os.path.join(ROOT, "tiled_attention_10_amd", "libtattn_clock.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    u64 = ctypes.c_ulonglong
+    L.tattn_clock_probe.argtypes = [u64, u64, ctypes.c_void_p, ctypes.c_void_p]
+    L.tattn_clock_probe.restype = ctypes.c_int
+    out = torch.zeros(2, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream(dev)
+    torch.cuda.synchronize()
+    if L.tattn_clock_probe(2_000_000, 10_000_000, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(side.cuda_stream)):
+        return None
+    for _ in range(launches):
+        fn()
+    torch.cuda.synchronize()
+    ticks, cycles = (int(x) for x in out.tolist())
+    return round(cycles / ticks * 0.1, 3) if ticks > 0 else None
 
 
 def fp8_rmse_leg(T, torch, W, dev, nrows=256):
@@ -351,6 +378,7 @@ def main():
         extra["ms_median"], extra["ms_min"] = launch_stats(torch, step_fn, args.steps, stream)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.dtype]
+    clock = measured_clock_ghz(torch, step_fn, dev)
 
     res = {
         "metric": "attention fwd TFLOPS (4·N²·d·H, causal/2)",
@@ -369,7 +397,9 @@ def main():
                    "causal": causal},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": recorded_traffic(kernel, wl_name),
-                     "kernel": kernel, "flop_per_launch": flops, "source_sha": source_hash(kernel)},
+                     "kernel": kernel, "flop_per_launch": flops, "source_sha": source_hash(kernel),
+                     "clock_ghz_measured": clock,
+                     "frac_at_measured_clock": round(tflops / (peak * clock / 2.4), 4) if clock else None},
         "wall_s_timed": round(wall, 3),
     }
     res.update(extra)

@@ -154,3 +154,19 @@ def test_python_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(T, "LIB_PATH", "/nonexistent/libtattn.so")
     with pytest.raises(ImportError):
         T.lib()
+
+
+def test_clock_probe_library():
+    # the benchmark's clock probe is a library of its own, outside the attention ABI
+    path = os.path.join(os.path.dirname(T.LIB_PATH), "libtattn_clock.so")
+    if not os.path.exists(path):
+        from tiled_attention_10_amd.build import build_probe
+        build_probe()
+    P = ctypes.CDLL(path)
+    u64 = ctypes.c_ulonglong
+    P.tattn_clock_probe.argtypes = [u64, u64, ctypes.c_void_p, ctypes.c_void_p]
+    # rejected before any launch
+    assert P.tattn_clock_probe(0, 10, ctypes.c_void_p(0x100000), None) == 1
+    assert P.tattn_clock_probe(10, 10, None, None) == 1
+    out = subprocess.run(["nm", "-D", "--defined-only", T.LIB_PATH], capture_output=True, text=True).stdout
+    assert "tattn_clock_probe" not in out

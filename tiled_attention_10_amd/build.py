@@ -42,8 +42,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(CSRC, "measure", "clock_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libtattn_clock.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The benchmark's shader-clock probe, a library of its own (not part of the ABI)."""
+    cmd = [_hipcc(), *FLAGS, "-shared", PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the clock probe:\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
+    """Compile every source and link the shared library (and the benchmark's clock
+    probe); returns the library's path."""
     os.makedirs(OBJDIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
@@ -55,6 +72,7 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 
