@@ -37,7 +37,10 @@ Modules:
   fp64 definition on the dequantised cache, per-sequence lengths, GQA
   (pinned by tests/test_oracle_decode.py: brute force, the causal prefill
   oracle's last row, torch float64 SDPA, block-boundary and planted mistakes).
-* ``fp8_attention`` -- fp64 emulation of the fp8 attention path.  PARITY
-  UNPINNED by the pages beyond their qualitative claim: it serves as a loose
-  sanity bound, the criterion being RMSE against the exact fp64 result.
+* ``fp8_attention`` -- fp64 emulation of the fp8 attention path.  The pages
+  give no worked FP8 result; it is pinned where nothing rounds (E4M3-exact
+  codes, power-of-two block scales, probabilities that are E4M3 powers of
+  two): there it must equal the plain definition (tests/test_oracle_fp8.py).
+  Elsewhere it serves as a sanity bound, the criterion being RMSE against the
+  exact fp64 result.
 """

@@ -1,10 +1,13 @@
 """fp64 emulation of the FP8 attention path (test infrastructure only).
 
-PARITY UNPINNED: the pages give no worked FP8 result, only the qualitative
-claim that incoherent processing lowers FP8 error ([FA3-card] "主要结果"), so
-this emulation is a loose sanity reference, not a definition.  The criterion
-for the FP8 path is its RMSE against ``attention.attention`` on the unquantised
-16-bit inputs, with and without rotation.
+The pages give no worked FP8 result, only the qualitative claim that
+incoherent processing lowers FP8 error ([FA3-card] "主要结果"), so this
+emulation is a sanity reference, not a definition.  It is pinned where no step
+rounds: with E4M3-exact codes, power-of-two block scales and scores whose
+probabilities (times their V factor) are E4M3 powers of two, it must equal
+``attention.attention`` on the dequantised values (tests/test_oracle_fp8.py).
+The criterion for the FP8 path is its RMSE against ``attention.attention`` on
+the unquantised 16-bit inputs, with and without rotation.
 
 Steps (the FP8 path's own, in order):
 

@@ -9,7 +9,8 @@
 * Quantiser: absmax scaling per (batch, head, 64-row block), saturation,
   zero blocks, ragged last block, and the rounding error bound of E4M3.
 * FP8 attention emulation: the direction the pages claim (rotation lowers the
-  error on outlier inputs); the emulation itself is "parity unpinned".
+  error on outlier inputs), and equality with the plain definition where no
+  step rounds (exact codes, power-of-two scales, power-of-two probabilities).
 """
 import math
 
@@ -200,3 +201,51 @@ def test_fp8_emulation_without_quantisation_error_is_exact():
     np.testing.assert_array_equal(o, np.zeros_like(o))
     qv = e4m3.decode(codes(q))
     assert np.array_equal(qv, q)
+
+
+def exact_probability_case(seed, N, Hq, Hkv, d, sk_max=2.0):
+    """E4M3 codes and power-of-two block scales for which the FP8 path rounds nothing.
+
+    Q and K codes are 0/1, so with softmax scale ln 2 every score is ln 2 times an
+    integer (sq·sk·popcount ≤ 16 with d = 4 and scales in {1, 2}).  exp(S − m) is
+    then 2^j with −16 ≤ j ≤ 0, and with V block scales in {1, 1/2} every rounded
+    probability 2^(j + 8 − kb) lies on an E4M3 value (2^−9 … 2^8).  Key 0 of
+    block 0 has all-one K codes and the largest K scale, so it holds every row's
+    maximum.  Returns codes, scales and the dequantised values the path
+    represents exactly.
+    """
+    rng = np.random.default_rng(seed)
+    nb = -(-N // 64)
+    qv = rng.integers(0, 2, (1, N, Hq, d)).astype(np.float64)
+    kv = rng.integers(0, 2, (1, N, Hkv, d)).astype(np.float64)
+    kv[0, 0] = 1.0
+    vv = rng.integers(-8, 9, (1, N, Hkv, d)).astype(np.float64)
+    sq = 2.0 ** rng.integers(0, 2, (1, Hq, nb))
+    sk = 2.0 ** rng.integers(0, 2, (1, Hkv, nb))
+    sk[:, :, 0] = sk_max
+    sv = np.ones((1, Hkv, nb))
+    sv[:, :, 1::2] = 0.5
+    rows = lambda s: np.repeat(s, 64, axis=2)[:, :, :N].transpose(0, 2, 1)[..., None]
+    vals = (qv * rows(sq), kv * rows(sk), vv * rows(sv))
+    codes = tuple(e4m3.encode(x) for x in (qv, kv, vv))
+    for c, x in zip(codes, (qv, kv, vv)):
+        assert np.array_equal(e4m3.decode(c), x)       # the codes are exact
+    scales = tuple(s.astype(np.float32) for s in (sq, sk, sv))
+    return codes, scales, vals
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_emulation_equals_definition_when_nothing_rounds(causal):
+    # Ragged last block (150 = 2·64 + 22), three V blocks with scales 1, 1/2, 1
+    # (the V scale folding into P̃ and back out of the denominator), GQA 4/2.
+    (q8, k8, v8), (sq, sk, sv), (q, k, v) = exact_probability_case(31, 150, 4, 2, 4)
+    scale = math.log(2.0)
+    want = A.attention(q, k, v, scale, causal)
+    got = fp8_attention_emul(q8, k8, v8, sq, sk, sv, scale=scale, causal=causal)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    rows = np.array([0, 1, 63, 64, 100, 149])
+    got_rows = fp8_attention_emul(q8, k8, v8, sq, sk, sv, scale=scale, causal=causal, rows=rows)
+    np.testing.assert_allclose(got_rows, want[:, rows], rtol=1e-12, atol=1e-12)
+    # The pin is sensitive: V scales taken as all ones move the result.
+    wrong = fp8_attention_emul(q8, k8, v8, sq, sk, np.ones_like(sv), scale=scale, causal=causal)
+    assert np.abs(wrong - want).max() > 1e-2
