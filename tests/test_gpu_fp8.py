@@ -5,9 +5,11 @@ output error is reported as RMSE against the exact fp64 attention of the
 unquantised 16-bit inputs, with and without the random-sign Hadamard rotation
 of Q and K, and the rotated RMSE must not exceed the unrotated one on inputs
 with outlier channels.  A sanity bound ties the kernel to the oracle's
-step-by-step emulation of the same quantisation (which is "parity unpinned":
-the pages give no worked FP8 result): RMSE(GPU, exact) <= 1.5 · RMSE(emulation,
-exact) + 1e-3.
+step-by-step emulation of the same quantisation (the pages give no worked FP8
+result): RMSE(GPU, exact) <= 1.5 · RMSE(emulation, exact) + 1e-3.  Where no
+step rounds (E4M3-exact inputs, power-of-two scales, probabilities that are
+E4M3 powers of two and partial sums on an exact grid) the kernel must equal
+exact attention up to the output rounding.
 """
 import math
 
@@ -200,3 +202,68 @@ def test_fp8_fp16_output_and_binding_checks():
         s64 = torch.ones(1, 2, 3, device=DEV)
         T.attn_fwd_fp8(q64, q64[:, :, :1].contiguous(), q64[:, :, :1].contiguous(), s64, s64[:, :1].contiguous(),
                        s64[:, :1].contiguous())
+
+
+def exact_fp8_inputs(seed, B, N, Hq, Hkv):
+    """E4M3 codes and power-of-two block scales on which the FP8 path rounds nothing.
+
+    Each query row has at most 2 one-codes (the rest 0), K codes are 0/1, so with
+    softmax scale ln 2 a score is ln 2 · sq · sk · (an integer ≤ 2) with scales in
+    {1, 2}: log2-unit scores are integers in [0, 8].  Key 0 has all-one K codes
+    and the largest K scale, so every row's maximum sits in the first key tile,
+    where the kernel's reference max is set and never moves.  Every probability
+    with its V factor (block scales 1 and 1/2, headroom 2^8) is then a power of
+    two between 2^-1 and 2^8, which E4M3 holds exactly, and every product with a
+    V code, and every partial sum up to 4096 keys, is a multiple of 2^-1 below
+    2^23.  That matters: the fp8 matrix cores truncate a dot product's small
+    terms below about 2^-14 of its largest one, and round their accumulation
+    toward zero, so wider score ranges are not exact there.  Returns the codes,
+    the scales and the values they stand for.
+    """
+    from oracle import e4m3
+    d = 128
+    rng = np.random.default_rng(seed)
+    nb = -(-N // 64)
+    qv = np.zeros((B, N, Hq, d))
+    np.put_along_axis(qv, rng.integers(0, d, (B, N, Hq, 2)), 1.0, axis=-1)
+    kv = rng.integers(0, 2, (B, N, Hkv, d)).astype(np.float64)
+    kv[:, 0] = 1.0
+    vv = rng.integers(-8, 9, (B, N, Hkv, d)).astype(np.float64)
+    sq = 2.0 ** rng.integers(0, 2, (B, Hq, nb))
+    sk = 2.0 ** rng.integers(0, 2, (B, Hkv, nb))
+    sk[:, :, 0] = 2.0
+    sv = np.ones((B, Hkv, nb))
+    sv[:, :, 1::2] = 0.5
+    per_row = lambda s: np.repeat(s, 64, axis=2)[:, :, :N].transpose(0, 2, 1)[..., None]
+    vals = (qv * per_row(sq), kv * per_row(sk), vv * per_row(sv))
+    codes = tuple(e4m3.encode(x) for x in (qv, kv, vv))
+    for c, x in zip(codes, (qv, kv, vv)):
+        assert np.array_equal(e4m3.decode(c), x)
+    return codes, tuple(s.astype(np.float32) for s in (sq, sk, sv)), vals
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1000, 8, 2), (2, 4096, 8, 1)], ids=lambda s: "B{}N{}H{}/{}".format(*s))
+def test_fp8_equals_exact_attention_when_nothing_rounds(shape, causal):
+    # With exact E4M3 inputs and exactly representable probabilities the FP8 path
+    # is exact attention up to fp32 accumulation and the fp16 output rounding.
+    B, N, Hq, Hkv = shape
+    (q8, k8, v8), (sq, sk, sv), (q, k, v) = exact_fp8_inputs(60 + N, B, N, Hq, Hkv)
+    scale = math.log(2.0)
+    print(f"[attn_fwd_fp8 exact-probability] B{B} N{N} H{Hq}/{Hkv} causal={causal}", flush=True)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    o, lse = T.attn_fwd_fp8(t(q8), t(k8), t(v8), t(sq), t(sk), t(sv), causal=causal, softmax_scale=scale,
+                            out_dtype=torch.float16, return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    rows = np.arange(N) if N <= 1000 else np.unique(np.concatenate(
+        [np.arange(0, 70), np.arange(N - 70, N), np.random.default_rng(N).choice(N, 200, replace=False)]))
+    want, want_lse = A.attention_rows(q, k, v, rows, scale, causal)
+    got = o[:, rows]
+    err = np.abs(got - want)
+    tol = 1.01 * 2.0 ** -11 * np.abs(want) + 2e-4
+    bad = np.argwhere(err > tol)
+    detail = [(int(rows[r]), int(h), int(c), float(got[b, r, h, c]), float(want[b, r, h, c]))
+              for b, r, h, c in bad[:8]]
+    assert len(bad) == 0, f"{len(bad)} elements off, max err {err.max():.3g}; (row, head, ch, got, want): {detail}"
+    np.testing.assert_allclose(lse[:, :, rows], want_lse, rtol=1e-5, atol=1e-5)
