@@ -236,3 +236,52 @@ def test_decode_full_size_sampled():
         ref, ref_lse = D.decode_attention(qs, kcs, kss, vcs, vss, [int(seqlens[b])], return_lse=True)
         check(o[b:b + 1, kv * g:(kv + 1) * g], lse[b:b + 1, kv * g:(kv + 1) * g], ref, ref_lse,
               vmax_per_head(vcs, vss, [int(seqlens[b])], g), "bf16")
+
+
+def exact_decode_inputs(seed, B, N, Hq, Hkv, dtype):
+    """A query and an E4M3 cache on which the decode step rounds nothing before the output.
+
+    Query rows have at most 2 entries of 1 (the rest 0) and K codes are 0/1 with
+    block scales 1 or 2, so with softmax scale ln 2 every score is an integer in
+    [0, 4] in log2 units.  The reference max is set on each wave's first step and
+    moves only when a score passes it by more than 8, so here it never moves
+    again: every probability is a power of two between 2^-4 and 2^4, exact in
+    both 16-bit types.  V codes are integers in [-4, 4] with block scales 1 or
+    1/2, so every product and per-chunk partial sum stays on a 2^-5 grid below
+    2^17, where fp32 accumulation is exact.
+    """
+    from oracle import e4m3
+    d = 128
+    rng = np.random.default_rng(seed)
+    nb = -(-N // 64)
+    q = np.zeros((B, Hq, d))
+    np.put_along_axis(q, rng.integers(0, d, (B, Hq, 2)), 1.0, axis=-1)
+    kv = rng.integers(0, 2, (B, N, Hkv, d)).astype(np.float64)
+    vv = rng.integers(-4, 5, (B, N, Hkv, d)).astype(np.float64)
+    ks = (2.0 ** rng.integers(0, 2, (B, Hkv, nb))).astype(np.float32)
+    vs = (2.0 ** -rng.integers(0, 2, (B, Hkv, nb))).astype(np.float32)
+    kc, vc = e4m3.encode(kv), e4m3.encode(vv)
+    assert np.array_equal(e4m3.decode(kc), kv) and np.array_equal(e4m3.decode(vc), vv)
+    q16 = W.to_torch(q.astype(np.float32), dtype)
+    assert np.array_equal(q16.double().numpy(), q)
+    return q16, kc, ks, vc, vs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("B,N,Hq,Hkv,lens", [(3, 4097, 16, 2, [4097, 1000, 70]), (1, 65536, 8, 1, [65536]),
+                                             (2, 9000, 64, 8, [9000, 8191])],
+                         ids=["ragged", "long", "gqa64"])
+def test_decode_equals_exact_attention_when_nothing_rounds(B, N, Hq, Hkv, lens, dtype):
+    # One chunk, many chunks (merge) and 4 query-head groups: the step must be the
+    # exact attention over the dequantised cache, rounded once to the query's type
+    # (plus a few fp32 roundings in the chunk merge).
+    import math
+    q16, kc, ks, vc, vs = exact_decode_inputs(80 + N, B, N, Hq, Hkv, dtype)
+    scale = math.log(2.0)
+    o, lse = run_gpu(q16, kc, ks, vc, vs, lens, scale)
+    ref, ref_lse = D.decode_attention(q16.double().numpy(), kc, ks, vc, vs, lens, scale, return_lse=True)
+    err = np.abs(o - ref)
+    tol = (1.01 * U[dtype] + 2.0 ** -16) * np.abs(ref) + 1e-6
+    bad = np.argwhere(err > tol)
+    assert len(bad) == 0, f"{len(bad)} elements off, max err {err.max():.3g}; first {[tuple(int(i) for i in x) for x in bad[:6]]}"
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-5, atol=1e-5)
