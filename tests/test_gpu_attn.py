@@ -229,6 +229,11 @@ def exact_16bit_inputs(seed, B, N, Hq, Hkv, d, dtype):
     tt = tuple(W.to_torch(x.astype(np.float32), dtype) for x in (q, k, v))
     for a, x in zip(tt, (q, k, v)):
         assert np.array_equal(a.double().numpy(), x)
+    check_rows = rng.choice(N, min(N, 64), replace=False)
+    for b in range(B):
+        for h in range(Hq):
+            s = q[b, check_rows, h] @ k[b, :, h // (Hq // Hkv)].T      # log2-unit scores
+            assert s.min() >= 0 and s.max() <= 8 and (s == s.round()).all() and (s.max(axis=1) == s[:, 0]).all()
     return tt, (q, k, v)
 
 

@@ -264,6 +264,12 @@ def exact_decode_inputs(seed, B, N, Hq, Hkv, dtype):
     assert np.array_equal(e4m3.decode(kc), kv) and np.array_equal(e4m3.decode(vc), vv)
     q16 = W.to_torch(q.astype(np.float32), dtype)
     assert np.array_equal(q16.double().numpy(), q)
+    per_row = np.repeat(ks, 64, axis=2)[:, :, :N]                     # [B, Hkv, N]
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // (Hq // Hkv)
+            s = (kv[b, :, kh] @ q[b, h]) * per_row[b, kh]              # log2-unit scores
+            assert s.min() >= 0 and s.max() <= 4 and (s == s.round()).all()
     return q16, kc, ks, vc, vs
 
 

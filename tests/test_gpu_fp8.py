@@ -239,6 +239,11 @@ def exact_fp8_inputs(seed, B, N, Hq, Hkv):
     codes = tuple(e4m3.encode(x) for x in (qv, kv, vv))
     for c, x in zip(codes, (qv, kv, vv)):
         assert np.array_equal(e4m3.decode(c), x)
+    check_rows = rng.choice(N, min(N, 64), replace=False)
+    for b in range(B):
+        for h in range(Hq):
+            s = vals[0][b, check_rows, h] @ vals[1][b, :, h // (Hq // Hkv)].T      # log2-unit scores
+            assert s.min() >= 0 and s.max() <= 8 and (s == s.round()).all() and (s.max(axis=1) == s[:, 0]).all()
     return codes, tuple(s.astype(np.float32) for s in (sq, sk, sv)), vals
 
 
