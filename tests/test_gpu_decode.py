@@ -245,10 +245,10 @@ def exact_decode_inputs(seed, B, N, Hq, Hkv, dtype):
     block scales 1 or 2, so with softmax scale ln 2 every score is an integer in
     [0, 4] in log2 units.  The reference max is set on each wave's first step and
     moves only when a score passes it by more than 8, so here it never moves
-    again: every probability is a power of two between 2^-4 and 2^4, exact in
-    both 16-bit types.  V codes are integers in [-4, 4] with block scales 1 or
-    1/2, so every product and per-chunk partial sum stays on a 2^-5 grid below
-    2^17, where fp32 accumulation is exact.
+    again: every probability, with its V block factor (scales 1 or 1/2) folded
+    in, is a power of two between 2^-5 and 2^4, exact in both 16-bit types.  V
+    codes are integers in [-4, 4], so every product and per-chunk partial sum
+    stays on a 2^-5 grid below 2^17, where fp32 accumulation is exact.
     """
     from oracle import e4m3
     d = 128
