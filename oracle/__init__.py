@@ -28,9 +28,11 @@ Modules:
 * ``hadamard``   -- Sylvester Hadamard matrix, fast Walsh–Hadamard transform,
   random-sign rotation (pinned by orthogonality and invariance tests).
 * ``quant``      -- per-(batch, head, 64-row block) absmax scaling and e4m3
-  codes, with the rounding decisions taken in fp32 (the kernel's precision).
+  codes, every decision taken on fp64 values by the definition: scale =
+  fl32(absmax/448), code = e4m3(y/scale) (pinned by exact rational brute
+  force over all codes and by orthogonal inputs that keep rows on the grid).
 * ``rope``       -- rotary position embedding (half-split pairs, caller's cos/sin
-  tables) ahead of the rotation and quantiser: the fused prologue of
+  tables) ahead of the rotation and quantiser, in fp64: the fused prologue of
   [FA3-card] "低精度优化" (pinned by tests/test_oracle_rope.py: identity,
   norms, composition, complex form, relative position, planted sign error).
 * ``decode``     -- one decode step over an FP8 block-quantised KV cache: the

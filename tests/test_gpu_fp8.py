@@ -4,12 +4,16 @@ The FP8 path is not an exact method, so (as the method's target states) its
 output error is reported as RMSE against the exact fp64 attention of the
 unquantised 16-bit inputs, with and without the random-sign Hadamard rotation
 of Q and K, and the rotated RMSE must not exceed the unrotated one on inputs
-with outlier channels.  A sanity bound ties the kernel to the oracle's
-step-by-step emulation of the same quantisation (the pages give no worked FP8
-result): RMSE(GPU, exact) <= 1.5 · RMSE(emulation, exact) + 1e-3.  Where no
-step rounds (E4M3-exact inputs, power-of-two scales, probabilities that are
-E4M3 powers of two and partial sums on an exact grid) the kernel must equal
-exact attention up to the output rounding.
+with outlier channels.  Three checks tie the kernel to the oracle:
+
+* every output element and every log-sum-exp lies within the bound derived
+  from E4M3's 2^-4 rounding of the probabilities around exact attention on the
+  dequantised codes the kernel received (tests/fp8_bounds.py);
+* RMSE(GPU, exact) <= 1.5 · RMSE(emulation, exact) + 1e-5, the emulation being
+  the oracle's step-by-step model of the same quantisation;
+* where no step rounds (E4M3-exact inputs, power-of-two scales, probabilities
+  that are E4M3 powers of two and partial sums on an exact grid) the kernel
+  equals exact attention up to the output rounding.
 """
 import math
 
@@ -17,6 +21,8 @@ import numpy as np
 import pytest
 import torch
 
+import fp8_bounds as FB
+import prologue_bounds as PB
 import tiled_attention_10_amd as T
 from oracle import attention as A
 from oracle import quant
@@ -29,6 +35,25 @@ DEV = "cuda:0"
 
 def rmse(a, b):
     return math.sqrt(float(np.mean((np.asarray(a, dtype=np.float64) - b) ** 2)))
+
+
+def rmse_bound(e_emul):
+    return 1.5 * e_emul + 1e-5
+
+
+def check_derived(o, codes, causal, rows=None, heads=None, lse=None, out_dtype="bf16", scale=None):
+    """O (and LSE) of the kernel within the E4M3-derived bound around exact attention on the
+    dequantised codes it received; returns the largest |Δ|/bound."""
+    O, L, bO, bL = FB.dq_reference(*codes, scale=scale, causal=causal, rows=rows, heads=heads, out_dtype=out_dtype)
+    sel = o if rows is None else o[:, rows]
+    sel = sel if heads is None else sel[:, :, heads]
+    r = FB.check(sel, O, bO, "O")
+    if lse is not None:
+        ls = lse if heads is None else lse[:, heads]
+        ls = ls if rows is None else ls[:, :, rows]
+        r = max(r, FB.check(ls, L, bL, "LSE"))
+    print(f"largest |Δ|/derived bound {r:.3f}")
+    return r
 
 
 def run_fp8(q8, k8, v8, sq, sk, sv, causal, out_dtype=torch.bfloat16, lse=False):
@@ -66,11 +91,8 @@ def test_fp8_small_shapes_against_emulation(shape, causal):
     assert np.isfinite(o).all()
     e_gpu, e_emul = rmse(o, exact), rmse(emul, exact)
     print(f"RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
-    assert e_gpu <= 1.5 * e_emul + 1e-3
-    assert np.abs(o - emul).max() <= 0.1
-    # the log-sum-exp comes from the fp8 scores (sanity bound only)
-    print(f"max |dLSE| {np.abs(lse - exact_lse).max():.3e}")
-    assert np.abs(lse - exact_lse).max() <= 0.5
+    assert e_gpu <= rmse_bound(e_emul)
+    check_derived(o, (q8, k8, v8, sq, sk, sv), causal, lse=lse)
 
 
 def test_fp8_uneven_persistent_shares():
@@ -85,15 +107,16 @@ def test_fp8_uneven_persistent_shares():
     e_gpu, e_emul = rmse(o[:, rows], exact), rmse(emul, exact)
     print(f"uneven shares: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
     assert np.isfinite(o).all()
-    assert e_gpu <= 1.5 * e_emul + 1e-3
+    assert e_gpu <= rmse_bound(e_emul)
+    check_derived(o, (q8, k8, v8, sq, sk, sv), False, rows=rows, heads=list(range(0, 40, 5)))
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_full_gqa_layer_sampled_rows(causal):
     # The benchmark's fp8 configuration: the 64/8-head 8k layer, Q and K rotated with the
-    # seeded signs and quantised (V quantised) by the GPU quantiser.  The oracle quantises
-    # one query head per KV group and all of K and V itself; the codes must agree bit for
-    # bit, and sampled rows are held to the emulation bound.
+    # seeded signs and quantised (V quantised) by the GPU quantiser.  Its codes are checked
+    # against the definition (one query head per KV group, all of K and V), and sampled rows
+    # of the output against the derived bound and the emulation's RMSE.
     w = W.WORKLOADS["gqa_bf16_h64kv8_n8192"]
     q, k, v = (W.to_torch(x, "bf16") for x in W.qkv_f32(w))
     s = W.rotation_signs(w.wid, w.d)
@@ -102,22 +125,25 @@ def test_fp8_full_gqa_layer_sampled_rows(causal):
     k8, sk = T.hadamard_rotate(k.to(DEV), sg, quantize=True)
     v8, sv = T.hadamard_rotate(v.to(DEV), None, quantize=True)
     print(f"[attn_fwd_fp8] full GQA layer causal={causal}", flush=True)
-    o = T.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal).float().cpu().numpy()
+    o, lse = T.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal, return_lse=True)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     heads = list(range(0, w.Hq, w.Hq // w.Hkv))                     # one per KV head
-    qo8, sqo = quant.quantize(q[:, :, heads].float().numpy(), s)
-    ko8, sko = quant.quantize(k.float().numpy(), s)
-    vo8, svo = quant.quantize(v.float().numpy(), None)
-    assert np.array_equal(q8[:, :, heads].cpu().numpy(), qo8) and np.array_equal(sq[:, heads].cpu().numpy(), sqo)
-    assert np.array_equal(k8.cpu().numpy(), ko8) and np.array_equal(sv.cpu().numpy(), svo)
+    codes = (q8[:, :, heads].cpu().numpy(), k8.cpu().numpy(), v8.cpu().numpy(),
+             sq[:, heads].cpu().numpy(), sk.cpu().numpy(), sv.cpu().numpy())
+    for x, c, sc, sgn in ((q[:, :, heads], codes[0], codes[3], s), (k, codes[1], codes[4], s), (v, codes[2], codes[5], None)):
+        y, e = PB.prologue_error(x.double().numpy(), sgn)
+        n_open, n = PB.check_codes(c, sc, y, e)
+        print(f"open codes {n_open}/{n}")
+        assert n_open <= 0.01 * n
     rows = np.unique(np.concatenate([[0, 63, 64, 255, 256, w.N - 1], np.random.default_rng(7).integers(0, w.N, 48)]))
-    emul = fp8_attention_emul(qo8, ko8, vo8, sqo, sko, svo, None, causal, rows=rows)
+    emul = fp8_attention_emul(*codes, None, causal, rows=rows)
     exact, _ = A.attention_rows(q[:, :, heads].contiguous(), k, v, rows, None, causal)
     got = o[:, rows][:, :, heads]
     e_gpu, e_emul = rmse(got, exact), rmse(emul, exact)
     print(f"full layer causal={causal}: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
     assert np.isfinite(o).all()
-    assert e_gpu <= 1.5 * e_emul + 1e-3
-    assert e_gpu < 0.1 * np.std(exact)
+    assert e_gpu <= rmse_bound(e_emul)
+    check_derived(o[:, :, heads], codes, causal, rows=rows, lse=lse[:, heads])
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -127,14 +153,15 @@ def test_fp8_maximum_sequence(causal):
     N = 262144
     q, k, v = (W.to_torch(x, "bf16") for x in W.random_qkv(43, 1, N, 2, 1, 128))
     q8, k8, v8, sq, sk, sv = quantise_all(q, k, v, None)
-    o = run_fp8(q8, k8, v8, sq, sk, sv, causal)
+    o, lse = run_fp8(q8, k8, v8, sq, sk, sv, causal, lse=True)
     rows = np.array([0, 1, 63, 64, 4095, 65536, N // 2 + 17, N - 65, N - 64, N - 1])
     exact, _ = A.attention_rows(q, k, v, rows, None, causal)
     emul = fp8_attention_emul(q8, k8, v8, sq, sk, sv, None, causal, rows=rows)
     e_gpu, e_emul = rmse(o[:, rows], exact), rmse(emul, exact)
     print(f"N={N} causal={causal}: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
     assert np.isfinite(o).all()
-    assert e_gpu <= 1.5 * e_emul + 1e-3
+    assert e_gpu <= rmse_bound(e_emul)
+    check_derived(o, (q8, k8, v8, sq, sk, sv), causal, rows=rows, lse=lse)
 
 
 def test_fp8_causal_row0_is_dequantised_v0():
@@ -168,24 +195,31 @@ def test_fp8_outlier_workload_rotation_reduces_error():
         emul = fp8_attention_emul(q8, k8, v8, sq, sk, sv, None, False, rows=rows)
         res[rot] = (rmse(o, exact), rmse(emul, exact))
         print(f"rotation={rot}: RMSE gpu {res[rot][0]:.4e}, emulation {res[rot][1]:.4e}")
-        assert res[rot][0] <= 1.5 * res[rot][1] + 1e-3
+        assert res[rot][0] <= rmse_bound(res[rot][1])
     assert res[True][0] <= res[False][0]
 
 
 def test_fp8_end_to_end_with_gpu_quantiser():
+    # GPU quantiser then GPU attention on the outlier workload: the codes follow the
+    # definition, the output is within the derived bound on the codes it received, and its
+    # error against the exact 16-bit attention is that of the oracle-quantised route.
     w, q, k, v, s = _c5_inputs()
     sg = torch.from_numpy(s).to(DEV)
     q8, sq = T.hadamard_rotate(q.to(DEV), sg, quantize=True)
     k8, sk = T.hadamard_rotate(k.to(DEV), sg, quantize=True)
     v8, sv = T.hadamard_rotate(v.to(DEV), None, quantize=True)
     o = T.attn_fwd_fp8(q8, k8, v8, sq, sk, sv).float().cpu().numpy()
-    rows = np.random.default_rng(6).integers(0, w.N, 128)
+    codes = tuple(t.cpu().numpy() for t in (q8, k8, v8, sq, sk, sv))
+    for x, c, sc, sgn in ((q, codes[0], codes[3], s), (k, codes[1], codes[4], s), (v, codes[2], codes[5], None)):
+        y, e = PB.prologue_error(x.double().numpy(), sgn)
+        assert PB.check_codes(c, sc, y, e)[0] <= 0.01 * x.numel()
+    rows = np.unique(np.random.default_rng(6).integers(0, w.N, 128))
+    check_derived(o, codes, False, rows=rows, heads=[0, 5, 15])
     exact, _ = A.attention_rows(q, k, v, rows)
-    ref8 = quantise_all(q, k, v, s)
-    o_ref = run_fp8(*ref8, False)
-    # the GPU quantiser reproduces the oracle's codes, so both routes agree exactly
-    assert np.array_equal(o, o_ref)
-    assert rmse(o[:, rows], exact) < 0.1 * np.std(exact)
+    o_ref = run_fp8(*quantise_all(q, k, v, s), False)
+    e_gpu, e_ref = rmse(o[:, rows], exact), rmse(o_ref[:, rows], exact)
+    print(f"RMSE GPU-quantised {e_gpu:.4e}, oracle-quantised {e_ref:.4e}")
+    assert abs(e_gpu - e_ref) <= 0.02 * e_ref
 
 
 def test_fp8_fp16_output_and_binding_checks():

@@ -1,21 +1,29 @@
-"""GPU parity of hadamard_rotate against the oracle, through the C ABI.
+"""GPU parity of hadamard_rotate against the oracle's fp64 definition, through the C ABI.
 
-The rotation's fp32 arithmetic is fully specified (butterfly stage order, one
-multiply by fl32(1/sqrt(d))), and so are the quantiser's divisions and
-rounding, so the outputs must match the oracle bit for bit: rotated values
-after rounding to the 16-bit type, E4M3 codes and fp32 block scales.
+The oracle decides every output on fp64 values (oracle/quant.py): the rotated
+row H_d·(s ⊙ x)/sqrt(d), rounded once to the 16-bit type, or the E4M3 code of
+y / fl32(absmax/448).  The kernel evaluates the rotation and the quantiser in
+fp32, so an output may differ only where the fp64 value lies within the fp32
+evaluation's error bound of a rounding boundary (tests/prologue_bounds.py).
+Each test requires the oracle's output everywhere else, requires every output
+to lie in its bounded interval, counts the elements the bound leaves open,
+prints the count and holds it below a small fraction.  Scales must be within
+the bound the block absmax's error allows, plus one ulp.
 """
 import numpy as np
 import pytest
 import torch
 
+import prologue_bounds as PB
 import tiled_attention_10_amd as T
-from oracle import quant
+from oracle import e4m3, quant
 from tiled_attention_10_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TDT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+# largest open fraction accepted: codes, and 16-bit outputs (fp16's grid is 8x finer)
+OPEN_CODES = 0.01
+OPEN_16 = {"bf16": 0.02, "fp16": 0.08}
 
 SHAPES = [(1, 1, 1, 64), (1, 64, 2, 128), (2, 130, 3, 64), (1, 1000, 4, 128), (2, 257, 16, 128)]
 
@@ -26,30 +34,30 @@ def _x(shape, dtype, seed):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}N{}H{}d{}".format(*s))
-def test_rotation_bit_exact(shape, dtype):
+def test_rotation_matches_definition(shape, dtype):
     x = _x(shape, dtype, sum(shape))
     s = W.rotation_signs(sum(shape), shape[-1])
     print(f"[hadamard_rotate] {shape} {dtype}", flush=True)
-    y = T.hadamard_rotate(x.to(DEV), torch.from_numpy(s).to(DEV)).cpu()
-    want = torch.from_numpy(quant.rotate_f32(x.float().numpy(), s)).to(TDT[dtype])
-    assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+    got = T.hadamard_rotate(x.to(DEV), torch.from_numpy(s).to(DEV)).cpu().double().numpy()
+    y, e = PB.prologue_error(x.double().numpy(), s)
+    n_open, n = PB.check_16bit(got, y, e, dtype)
+    print(f"open roundings {n_open}/{n}")
+    assert n_open <= OPEN_16[dtype] * n
 
 
 @pytest.mark.parametrize("rotate", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}N{}H{}d{}".format(*s))
-def test_quantisation_bit_exact(shape, dtype, rotate):
+def test_quantisation_matches_definition(shape, dtype, rotate):
     x = _x(shape, dtype, 7 * sum(shape))
     s = W.rotation_signs(3 + sum(shape), shape[-1]) if rotate else None
     print(f"[hadamard_rotate quant] {shape} {dtype} rotate={rotate}", flush=True)
     codes, scales = T.hadamard_rotate(x.to(DEV), None if s is None else torch.from_numpy(s).to(DEV),
                                       quantize=True)
-    want_codes, want_scales = quant.quantize(x.float().numpy(), s)
-    assert np.array_equal(scales.cpu().numpy(), want_scales)
-    got = codes.cpu().numpy()
-    mism = np.argwhere(got != want_codes)
-    assert len(mism) == 0, f"{len(mism)} code mismatches, first at {mism[:5].tolist()}: " \
-                           f"{got[tuple(mism[0])]:#x} vs {want_codes[tuple(mism[0])]:#x}"
+    y, e = PB.prologue_error(x.double().numpy(), s)
+    n_open, n = PB.check_codes(codes.cpu().numpy(), scales.cpu().numpy(), y, e)
+    print(f"open codes {n_open}/{n}")
+    assert n_open <= OPEN_CODES * n
 
 
 def test_identity_copy_and_outlier_workload():
@@ -59,6 +67,10 @@ def test_identity_copy_and_outlier_workload():
     assert torch.equal(y, q)
     s = W.rotation_signs(w.wid, w.d)
     codes, scales = T.hadamard_rotate(k.to(DEV), torch.from_numpy(s).to(DEV), quantize=True)
-    want_codes, want_scales = quant.quantize(k.float().numpy(), s)
-    assert np.array_equal(scales.cpu().numpy(), want_scales)
-    assert np.array_equal(codes.cpu().numpy(), want_codes)
+    yk, ek = PB.prologue_error(k.double().numpy(), s)
+    n_open, n = PB.check_codes(codes.cpu().numpy(), scales.cpu().numpy(), yk, ek)
+    print(f"outlier workload K: open codes {n_open}/{n}")
+    assert n_open <= OPEN_CODES * n
+    # and the oracle's codes of the same tensor agree with the GPU's outside the open set
+    oc, _ = quant.quantize(k.double().numpy(), s)
+    assert (e4m3.decode(codes.cpu().numpy()) != e4m3.decode(oc)).sum() <= n_open

@@ -114,25 +114,33 @@ def test_rotation_is_orthogonal_and_leaves_attention_unchanged():
     assert np.abs(A.attention(Hd.rotate(q, s2), kr, v) - A.attention(q, k, v)).max() > 1e-3
 
 
-def test_rotate_f32_matches_fp64_definition():
-    x = W.to_torch(W.normal(22, 0, (2, 70, 3, 128)), "bf16").float().numpy()
-    s = W.rotation_signs(22, 128)
-    np.testing.assert_allclose(quant.rotate_f32(x, s), Hd.rotate(x, s), rtol=0, atol=2e-5)
+def _fl32_nearest(fr):
+    """The fp32 value nearest to the rational ``fr`` (ties to even), found by exact comparison."""
+    from fractions import Fraction
+    c = np.float32(float(fr))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    dist = [abs(Fraction(float(x)) - fr) for x in cands]
+    best = min(dist)
+    picks = [x for x, dd in zip(cands, dist) if dd == best]
+    return picks[0] if len(picks) == 1 else [x for x in picks if not (x.view(np.uint32) & 1)][0]
 
 
 def test_block_scales_and_codes():
+    # scale = fl32(absmax/448) from the exact quotient; every code is the E4M3 value nearest to
+    # y/scale, found by brute force over all codes against y itself (|decode(c)·scale − y|)
+    from fractions import Fraction
     x = W.to_torch(W.normal(23, 0, (2, 130, 3, 64)), "bf16").float().numpy()
     x[1, 64:128, 2] = 0.0                               # an all-zero block
     codes, scales = quant.quantize(x)
     assert codes.dtype == np.uint8 and scales.dtype == np.float32
     assert scales.shape == (2, 3, 3)
-    amax = np.abs(x).reshape(2, 130, 3, 64)
+    table = e4m3.decode_table()[:0x7F]
     for b in range(2):
         for h in range(3):
             for blk in range(3):
                 rows = slice(64 * blk, min(130, 64 * blk + 64))
                 a = np.abs(x[b, rows, h]).max()
-                want = np.float32(a) / np.float32(448) if a > 0 else np.float32(1)
+                want = _fl32_nearest(Fraction(float(a)) / 448) if a > 0 else np.float32(1)
                 assert scales[b, h, blk] == want
                 c = codes[b, rows, h] & 0x7F
                 assert c.max() <= 0x7E
@@ -140,7 +148,32 @@ def test_block_scales_and_codes():
                     assert c.max() == 0x7E                 # the absmax element maps to ±448
                 else:
                     assert (c == 0).all()
-    assert amax.size
+                sc = float(scales[b, h, blk])
+                for y, got in zip(x[b, rows, h].ravel()[::7], codes[b, rows, h].ravel()[::7]):
+                    dist = [abs(Fraction(float(t)) * Fraction(sc) - Fraction(abs(float(y)))) for t in table]
+                    best = min(dist)
+                    ties = [i for i, dd in enumerate(dist) if dd == best]
+                    want_c = ties[0] if len(ties) == 1 else [i for i in ties if i % 2 == 0][0]
+                    assert got & 0x7F == want_c and (got >> 7) == (1 if np.signbit(y) else 0)
+
+
+def test_quantiser_of_rotated_rows_decides_on_fp64_values():
+    # rotation by an orthogonal map that keeps a row on the E4M3 grid: with signs +1 and a row
+    # that is a multiple of a Hadamard row, the rotated row has one nonzero channel, so every
+    # code is 0 except the absmax channel's 0x7E, whatever the fp32 rounding would have been
+    d = 128
+    H = scipy.linalg.hadamard(d).astype(np.float64)
+    x = np.zeros((1, 64, 1, d))
+    for n in range(64):
+        x[0, n, 0] = H[n % d] * (1 + n) / 8.0
+    codes, scales = quant.quantize(x, np.ones(d))
+    y = Hd.rotate(x, np.ones(d))
+    assert np.count_nonzero(np.abs(y) > 1e-9) == 64
+    nz = codes != 0
+    assert nz.sum() == 64 and (codes[nz] & 0x7F).max() == 0x7E
+    # the absmax row (n = 63) maps to 448 exactly; row n maps to 448·(n+1)/64 rounded to E4M3
+    vals = e4m3.decode(codes[nz]) * float(scales[0, 0, 0])
+    np.testing.assert_allclose(np.sort(np.abs(vals)), np.sort(np.abs(y[np.abs(y) > 1e-9])), rtol=2.0 ** -4)
 
 
 def test_dequantisation_error_bound():
@@ -151,18 +184,6 @@ def test_dequantisation_error_bound():
     # E4M3 round-to-nearest: relative 2^-4 for normals, absolute 2^-10 below 2^-6
     bound = np.maximum(np.abs(x) * 2.0 ** -4, per_row * 2.0 ** -10) * (1 + 1e-6)
     assert (np.abs(deq - x) <= bound).all()
-
-
-def test_quantised_rotation_codes_use_fp32_decisions():
-    x = W.to_torch(W.normal(25, 0, (1, 64, 1, 128)), "bf16").float().numpy()
-    s = W.rotation_signs(25, 128)
-    codes, scales = quant.quantize(x, s)
-    y = quant.rotate_f32(x, s)
-    amax = np.abs(y).max()
-    assert scales[0, 0, 0] == amax / np.float32(448)
-    q = (y * (np.float32(448) / amax)).astype(np.float32)
-    assert q.dtype == np.float32
-    np.testing.assert_array_equal(codes, e4m3.encode(q))
 
 
 def _c5_like(seed, N=512, H=2):
@@ -249,3 +270,25 @@ def test_fp8_emulation_equals_definition_when_nothing_rounds(causal):
     # The pin is sensitive: V scales taken as all ones move the result.
     wrong = fp8_attention_emul(q8, k8, v8, sq, sk, np.ones_like(sv), scale=scale, causal=causal)
     assert np.abs(wrong - want).max() > 1e-2
+
+
+@pytest.mark.parametrize("rot,causal", [(False, False), (True, False), (True, True)])
+def test_fp8_emulation_within_derived_bound_of_dequantised_definition(rot, causal):
+    # The emulation's weights are the E4M3 roundings of p·f, so it must sit inside the bound
+    # derived from E4M3's 2^-4 (tests/fp8_bounds.py) around exact attention on the dequantised
+    # codes, for O and for the log-sum-exp.
+    import fp8_bounds as FB
+    q, k, v, s = _c5_like(2, N=384)
+    sg = s if rot else None
+    (q8, sq), (k8, sk), (v8, sv) = quant.quantize(q, sg), quant.quantize(k, sg), quant.quantize(v)
+    rows = np.array([0, 1, 63, 64, 200, 383])
+    O, lse, bO, blse = FB.dq_reference(q8, k8, v8, sq, sk, sv, causal=causal, rows=rows)
+    emul = fp8_attention_emul(q8, k8, v8, sq, sk, sv, causal=causal, rows=rows)
+    assert FB.check(emul, O, bO, "emulation") < 1.0
+    # the bound is not vacuous: it is well below the spread of O, and a planted mistake (V block
+    # scales dropped from the folded factor) leaves it
+    assert np.median(bO) < 0.1 * np.std(O)
+    sv_wrong = np.where(np.arange(sv.shape[-1]) % 2 == 0, sv, 4 * sv).astype(np.float32)
+    wrong = fp8_attention_emul(q8, k8, v8, sq, sk, sv_wrong, causal=causal, rows=rows)
+    with pytest.raises(AssertionError):
+        FB.check(wrong, O, bO, "planted")

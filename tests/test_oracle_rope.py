@@ -117,26 +117,17 @@ def test_hadamard_after_rope_keeps_scores():
     assert np.allclose(sq, q[0, :, 0] @ k[0, :, 0].T, rtol=0, atol=1e-10)
 
 
-def test_f32_emulation_tracks_fp64():
-    d, N = 128, 33
-    x = rng(14).standard_normal((2, N, 3, d)).astype(np.float32)
-    c, s, _ = random_tables(15, N, d)
-    c32, s32 = c.astype(np.float32), s.astype(np.float32)
-    exact = R.rope(x, c32, s32)                 # fp64 arithmetic on the same fp32 inputs
-    got = R.rope_f32(x, c32, s32)
-    # each output is fl(fl(p1) ± fl(p2)): |error| <= 2^-23 · (|p1| + |p2|) with u = 2^-24
-    a, b = x[..., :64].astype(np.float64), x[..., 64:].astype(np.float64)
-    cc, ss = c32[None, :, None, :].astype(np.float64), s32[None, :, None, :].astype(np.float64)
-    bound = 2.0 ** -23 * np.concatenate([np.abs(a * cc) + np.abs(b * ss), np.abs(b * cc) + np.abs(a * ss)], -1)
-    assert (np.abs(got - exact) <= bound).all()
-
-
-def test_fused_quantiser_matches_two_step_route():
+def test_fused_quantiser_is_the_quantiser_of_the_embedded_rows():
+    # the fused route decides on the same fp64 values as embedding first, then quantising
     d, N = 128, 130
     x = rng(16).standard_normal((1, N, 2, d)).astype(np.float32)
     c, s, _ = random_tables(17, N, d)
     c32, s32 = c.astype(np.float32), s.astype(np.float32)
     signs = np.where(rng(18).random(d) < 0.5, -1, 1).astype(np.int8)
     codes, scales = R.quantize_rope(x, c32, s32, signs)
-    codes2, scales2 = quant.quantize(R.rope_f32(x, c32, s32), signs)
+    codes2, scales2 = quant.quantize(R.rope(x, c32, s32), signs)
     assert np.array_equal(codes, codes2) and np.array_equal(scales, scales2)
+    np.testing.assert_array_equal(R.rope_rotate(x, c32, s32, signs), Hd.rotate(R.rope(x, c32, s32), signs))
+    # a rotation by the wrong angle (sin negated) moves the codes
+    codes3, _ = R.quantize_rope(x, c32, -s32, signs)
+    assert (codes3 != codes).mean() > 0.5
