@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--causal 0|1]
                     [--dtype bf16|fp16|fp8] [--no-cpu-baseline] [--no-fp8] [--no-decode]
-                    [--copy-calibration]
+                    [--no-configs] [--variant NAME] [--ablation] [--copy-calibration]
 
 A step is one attention forward over the workload's synthetic Q, K, V, already
 resident in HBM.  The default workload is one layer of a 70B-class model with
@@ -27,6 +27,16 @@ one decode step over an FP8 KV cache (B=4 sequences of up to
 131072 cached tokens, 64 query heads over 8 KV heads; "decode" in the JSON line, HBM roofline
 on algorithmic bytes); --workload decode_fp8kv_b4_h64kv8_n131072 makes the decode step the
 benchmarked step (GB/s, with the decode oracle timed on one sequence's KV head).
+
+The default run also times every other workload of the method's configurations
+once each ("configs": MHA fp16 2k non-causal and causal, the 8k GQA layer causal,
+the 128k causal prefill, and the fp8 outlier workload with and without rotation
+next to bf16 on the same inputs), with ms, TFLOPS and fraction of peak.
+
+--variant NAME routes every call through a scheduling variant of the library
+(libtattn_NAME.so, built by build.py).  --ablation times the workload with the
+shipped library and every variant, interleaved over rounds, and prints one JSON
+line with each variant's median time and its change against the shipped build.
 
 --copy-calibration runs only a plain device copy of known size (for scaling
 the FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exits.
@@ -67,6 +77,10 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows per head in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg of the default run")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' legs")
+    ap.add_argument("--variant", default=None, help="time a scheduling variant of the library instead")
+    ap.add_argument("--ablation", action="store_true", help="time the shipped library against every variant")
+    ap.add_argument("--rounds", type=int, default=4, help="interleaved rounds of --ablation")
     return ap.parse_args()
 
 
@@ -311,6 +325,90 @@ def decode_bench(T, torch, W, name, steps, warmup, stream, dev, cpu=True):
     return res
 
 
+def _tf(flops, ms):
+    return round(flops / (ms * 1e-3) / 1e12, 2)
+
+
+def config_legs(T, torch, W, stream, dev, steps=10, warmup=10):
+    """Each remaining workload of the method's configurations timed once (inputs resident
+    in HBM): ms per launch (mean over ``steps`` after ``warmup``), TFLOPS, fraction of peak."""
+    out = {}
+
+    def leg(name, fn, flops, peak_key, **kw):
+        ms, _ = time_launches(torch, fn, steps, warmup, stream)
+        out[name] = {"ms": round(ms, 4), "tflops": _tf(flops, ms),
+                     "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[peak_key], 4), **kw}
+        print(f"[bench] config {name}: {ms:.4f} ms", file=sys.stderr, flush=True)
+        return ms
+
+    w = W.WORKLOADS["mha_fp16_b4_h16_n2048"]
+    q, k, v = (W.to_torch(x, "fp16").to(dev) for x in W.qkv_f32(w))
+    o = torch.empty_like(q)
+    for c in (False, True):
+        leg(f"{w.name}_{'causal' if c else 'noncausal'}", lambda: T.attn_fwd(q, k, v, causal=c, out=o),
+            w.flops(c), "fp16", dtype="fp16")
+    w = W.WORKLOADS["gqa_bf16_h64kv8_n8192"]
+    q, k, v = (W.to_torch(x, "bf16").to(dev) for x in W.qkv_f32(w))
+    o = torch.empty_like(q)
+    leg(f"{w.name}_causal", lambda: T.attn_fwd(q, k, v, causal=True, out=o), w.flops(True), "bf16", dtype="bf16")
+    w = W.WORKLOADS["long_bf16_h8kv1_n131072"]
+    q, k, v = (W.to_torch(x, "bf16").to(dev) for x in W.qkv_f32(w))
+    o = torch.empty_like(q)
+    leg(f"{w.name}_causal", lambda: T.attn_fwd(q, k, v, causal=True, out=o), w.flops(True), "bf16",
+        dtype="bf16")
+    del q, k, v, o
+    w = W.WORKLOADS["fp8_outlier_b2_h16_n4096"]
+    q, k, v = (W.to_torch(x, "bf16").to(dev) for x in W.qkv_f32(w))
+    o = torch.empty_like(q)
+    f = w.flops(False)
+    ms16 = leg(f"{w.name}_bf16", lambda: T.attn_fwd(q, k, v, out=o), f, "bf16", dtype="bf16")
+    signs = torch.from_numpy(W.rotation_signs(w.wid, w.d)).to(dev)
+    for rot in (False, True):
+        sg = signs if rot else None
+        q8, sq = T.hadamard_rotate(q, sg, quantize=True)
+        k8, sk = T.hadamard_rotate(k, sg, quantize=True)
+        v8, sv = T.hadamard_rotate(v, None, quantize=True)
+        name = f"{w.name}_fp8_{'with' if rot else 'without'}_hadamard"
+        ms8 = leg(name, lambda: T.attn_fwd_fp8(q8, k8, v8, sq, sk, sv, out=o), f, "fp8", dtype="fp8")
+        out[name]["speedup_vs_bf16"] = round(ms16 / ms8, 3)
+    return out
+
+
+def ablation(args, T, torch, W, stream, dev):
+    """The workload timed with the shipped library and each scheduling variant, in
+    interleaved rounds (shipped, v1, v2, ..., shipped, v1, ...), median over rounds."""
+    import statistics
+    from tiled_attention_10_amd.build import VARIANTS
+
+    w = W.WORKLOADS[args.workload]
+    causal = bool(args.causal)
+    dt = "bf16" if args.dtype == "fp8" else args.dtype
+    q, k, v = (W.to_torch(x, dt).to(dev) for x in W.qkv_f32(w))
+    o = torch.empty_like(q)
+    names = ["shipped"] + sorted(VARIANTS)
+    times = {n: [] for n in names}
+    for r in range(args.rounds):
+        for n in names:
+            path = T.LIB_PATH if n == "shipped" else T.variant_path(n)
+            with T.use_library(path):
+                ms, _ = time_launches(torch, lambda: T.attn_fwd(q, k, v, causal=causal, out=o), args.steps,
+                                      args.warmup, stream)
+            times[n].append(ms)
+            print(f"[ablation] round {r} {n}: {ms:.4f} ms", file=sys.stderr, flush=True)
+    flops = w.flops(causal)
+    base = statistics.median(times["shipped"])
+    res = {"metric": "attention fwd TFLOPS per scheduling variant (4·N²·d·H, causal/2)", "unit": "TFLOPS",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "rounds": args.rounds, "dtype": dt,
+           "config": {"workload": w.name + ("_causal" if causal else "_noncausal"), "B": w.B, "N": w.N,
+                      "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": causal},
+           "variants": {}}
+    for n in names:
+        m = statistics.median(times[n])
+        res["variants"][n] = {"ms_median": round(m, 4), "ms_rounds": [round(t, 4) for t in times[n]],
+                              "tflops": _tf(flops, m), "delta_vs_shipped": round(base / m - 1, 4)}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -323,6 +421,12 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.ablation:
+        print(json.dumps(ablation(args, T, torch, W, stream, dev)), flush=True)
+        return
+    if args.variant is not None:
+        # every call below goes through the variant build of the library
+        T.use_library(T.variant_path(args.variant)).__enter__()
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -394,7 +498,7 @@ def main():
         "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": wl_name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
-                   "causal": causal},
+                   "causal": causal, **({"variant": args.variant} if args.variant else {})},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": recorded_traffic(kernel, wl_name),
                      "kernel": kernel, "flop_per_launch": flops, "source_sha": source_hash(kernel),
@@ -421,11 +525,13 @@ def main():
                       "frac_of_fp8_peak": round(flops / (fms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                       "prologue_ms": round(pms, 4), "speedup_vs_" + args.dtype: round(ms / fms, 3),
                       "speedup_incl_prologue": round(ms / (fms + pms), 3)}
-    if args.dtype != "fp8" and not args.no_fp8:
-        res["fp8_rmse"] = fp8_rmse_leg(T, torch, W, dev)
+    if not args.no_configs:
+        res["configs"] = config_legs(T, torch, W, stream, dev)
     if not args.no_decode:
         res["decode"] = decode_bench(T, torch, W, "decode_fp8kv_b4_h64kv8_n131072", args.steps, args.warmup,
                                      stream, dev, cpu=False)
+    if args.dtype != "fp8" and not args.no_fp8:
+        res["fp8_rmse"] = fp8_rmse_leg(T, torch, W, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(q, k, v, causal, args.cpu_rows, w.wid)
     print(json.dumps(res), flush=True)

@@ -69,6 +69,8 @@ enum {
  *                                         masked scores)
  *   B, N, Hq, Hkv >= 1 with Hq % Hkv == 0; query head h reads key/value
  *   head h / (Hq/Hkv).  d ∈ {64, 128}.  Any N (a partial last tile is masked).
+ *   64 key rows must span less than 4 GiB: Hkv·d·2·64 < 2^32 (Hkv·d·64 on
+ *   the fp8 path), else TATTN_ERR_INVALID_ARG.
  *   softmax_scale: finite and > 0 (1/sqrt(d) for the standard definition).
  *   causal: 0 or 1.  dtype: TATTN_F16 or TATTN_BF16 (output in the same type).
  */
@@ -123,7 +125,11 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  *                                         fp32 multiply per element; nearest-even,
  *                                         saturating at ±448; y · 1 for a zero block)
  * and ``y`` receives uint8 codes [B, N, H, d], ``scales_out`` fp32
- * [B, H, ceil(N/64)].
+ * [B, H, ceil(N/64)].  With exact arithmetic this is the definition
+ * scale = absmax/448, code = nearest E4M3 value of y/scale; the fp32 evaluation
+ * can differ from it only where y/scale lies within its rounding error of an
+ * E4M3 rounding boundary, and a 16-bit y only where y lies that close to a
+ * 16-bit rounding boundary.
  *
  *   x          [B, N, H, d] in_dtype (TATTN_F16 or TATTN_BF16) (read)
  *   y          output as above; must not alias x

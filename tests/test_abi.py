@@ -67,20 +67,23 @@ def fwd(L, q=P, k=P, v=P, o=P, lse=None, B=1, N=128, Hq=2, Hkv=1, d=128, scale=0
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(causal=2), INVALID),
     (dict(q=BAD), MISALIGNED), (dict(v=BAD), MISALIGNED), (dict(o=P + 8), MISALIGNED),
     (dict(lse=P + 2), MISALIGNED), (dict(B=1 << 20, N=1 << 20, Hq=64, Hkv=8), INVALID),
+    # 64 key rows of 2^18 KV heads of 256 bytes span 4 GiB: past the kernels' 32-bit tile offsets
+    (dict(Hq=1 << 18, Hkv=1 << 18, N=1), INVALID),
 ])
 def test_attn_fwd_rejects(L, kw, status):
     assert fwd(L, **kw) == status
     assert L.tattn_last_error() != b""
 
 
-def fp8(L, d=128, out_dtype=2, scales=P, causal=0, q8=P, N=128):
-    return L.attn_fwd_fp8(q8, P, P, scales, P, P, P, None, 1, N, 2, 2, d, 0.1, causal, out_dtype, None)
+def fp8(L, d=128, out_dtype=2, scales=P, causal=0, q8=P, N=128, Hq=2, Hkv=2):
+    return L.attn_fwd_fp8(q8, P, P, scales, P, P, P, None, 1, N, Hq, Hkv, d, 0.1, causal, out_dtype, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(d=64), UNSUPPORTED), (dict(out_dtype=7), UNSUPPORTED), (dict(scales=None), INVALID),
     (dict(causal=-1), INVALID), (dict(q8=BAD), MISALIGNED), (dict(scales=P + 1), MISALIGNED),
     (dict(q8=None), INVALID), (dict(N=-5), INVALID), (dict(N=262145), UNSUPPORTED),
+    (dict(Hq=1 << 19, Hkv=1 << 19, N=1), INVALID),
 ])
 def test_attn_fwd_fp8_rejects(L, kw, status):
     assert fp8(L, **kw) == status

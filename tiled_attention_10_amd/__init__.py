@@ -8,12 +8,14 @@ raises: there is no fallback implementation.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
 
 __all__ = ["attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "attn_decode_fp8kv",
-           "decode_workspace_size", "TattnError", "lib", "LIB_PATH", "TATTN_F16", "TATTN_BF16"]
+           "decode_workspace_size", "TattnError", "lib", "LIB_PATH", "TATTN_F16", "TATTN_BF16",
+           "use_library", "variant_path"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtattn.so")
 
@@ -30,33 +32,60 @@ class TattnError(RuntimeError):
         self.status = status
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m tiled_attention_10_amd.build`")
+    L = ctypes.CDLL(path)
+    _declare(L)
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Load libtattn.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tiled_attention_10_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
-        L.attn_fwd.restype = i
-        L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
-        L.attn_fwd_fp8.restype = i
-        L.hadamard_rotate.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
-        L.hadamard_rotate.restype = i
-        L.rope_hadamard_rotate.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
-        L.rope_hadamard_rotate.restype = i
-        L.attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                                         i, i, i, i, i, f, i, vp]
-        L.attn_decode_fp8kv.restype = i
-        L.attn_decode_fp8kv_workspace_size.argtypes = [i, i, i, i, i]
-        L.attn_decode_fp8kv_workspace_size.restype = ctypes.c_size_t
-        L.tattn_status_string.argtypes = [i]
-        L.tattn_status_string.restype = ctypes.c_char_p
-        L.tattn_last_error.argtypes = []
-        L.tattn_last_error.restype = ctypes.c_char_p
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def variant_path(name: str) -> str:
+    """Path of a scheduling variant of the library (``libtattn_<name>.so``, built by build.py)."""
+    return os.path.join(os.path.dirname(LIB_PATH), f"libtattn_{name}.so")
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Route this module's calls through another build of the same ABI (a scheduling
+    variant of the kernels) for the duration of the block."""
+    global _lib
+    saved = lib()
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _declare(L: ctypes.CDLL) -> None:
+    """Argument and result types of the exported functions."""
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.attn_fwd.restype = i
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.attn_fwd_fp8.restype = i
+    L.hadamard_rotate.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    L.hadamard_rotate.restype = i
+    L.rope_hadamard_rotate.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    L.rope_hadamard_rotate.restype = i
+    L.attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                     i, i, i, i, i, f, i, vp]
+    L.attn_decode_fp8kv.restype = i
+    L.attn_decode_fp8kv_workspace_size.argtypes = [i, i, i, i, i]
+    L.attn_decode_fp8kv_workspace_size.restype = ctypes.c_size_t
+    L.tattn_status_string.argtypes = [i]
+    L.tattn_status_string.restype = ctypes.c_char_p
+    L.tattn_last_error.argtypes = []
+    L.tattn_last_error.restype = ctypes.c_char_p
 
 
 def _check(status: int) -> None:

@@ -24,16 +24,31 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
 SOURCES = ["attn_fwd16.hip", "attn_fwd_fp8.hip", "attn_decode.hip", "hadamard.hip", "api.cpp"]
 
+# Scheduling variants of the 16-bit kernel for the ablation: each is the whole
+# library with attn_fwd16.hip rebuilt under other schedule settings, written to
+# libtattn_<name>.so.  The shipped library uses the defaults in attn_fwd16.hip
+# (4-stage rings, reads 2 products ahead, two-group ping-pong, split loads).
+VARIANTS = {
+    "stages3": ["-DTATTN_STAGES=3"],
+    "stages5": ["-DTATTN_STAGES=5"],
+    "uniform": ["-DTATTN_PINGPONG=0"],
+    "readahead1": ["-DTATTN_READ_AHEAD=1"],
+    "readahead4": ["-DTATTN_READ_AHEAD=4"],
+    "loads_at_barrier": ["-DTATTN_SPLIT_LOADS=0"],
+}
+
 
 def _hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, variant: str | None = None) -> str:
+    stem = os.path.splitext(src)[0] + ("" if variant is None else "_" + variant)
+    obj = os.path.join(OBJDIR, stem + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [] if variant is None else VARIANTS[variant]
+    cmd = [_hipcc(), *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,23 +73,83 @@ def build_probe(verbose: bool = False) -> str:
     return PROBE_LIB
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library (and the benchmark's clock
-    probe); returns the library's path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def variant_lib(name: str) -> str:
+    return os.path.join(PKG, f"libtattn_{name}.so")
+
+
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, variants: bool = True) -> str:
+    """Compile every source and link the shared library, the scheduling variants
+    (unless ``variants`` is False) and the benchmark's clock probe; returns the
+    library's path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = [(s, None) for s in SOURCES] + ([("attn_fwd16.hip", v) for v in VARIANTS] if variants else [])
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    base = objs[:len(SOURCES)]
+    _link(base, LIB, verbose)
+    for i, v in enumerate(VARIANTS if variants else []):
+        _link([objs[len(SOURCES) + i]] + base[1:], variant_lib(v), verbose)
     build_probe(verbose)
     return LIB
 
 
+def resource_usage(verbose: bool = False, sources=None) -> str:
+    """Per-kernel register, scratch, occupancy and LDS use of the given sources (default
+    all) and, with attn_fwd16.hip, its scheduling variants, from the compiler's
+    kernel-resource-usage remarks (a markdown table)."""
+    import re
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = [s for s in SOURCES if s.endswith(".hip") and (not sources or s in sources)]
+    jobs = [(s, None) for s in srcs] + ([("attn_fwd16.hip", v) for v in VARIANTS] if "attn_fwd16.hip" in srcs else [])
+
+    def one(job):
+        src, var = job
+        extra = [] if var is None else VARIANTS[var]
+        cmd = [_hipcc(), *FLAGS, *extra, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+               "-o", os.path.join(OBJDIR, "resource_usage_tmp_" + (var or "") + os.path.splitext(src)[0] + ".o")]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        rows, cur = [], None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark:\s+(Function Name|VGPRs|AGPRs|TotalSGPRs|ScratchSize \[bytes/lane\]|"
+                          r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]): (\S+)", line)
+            if not m:
+                continue
+            key, val = m.group(1).split(" [")[0], m.group(2)
+            if key == "Function Name":
+                cur = {"kernel": val}
+                rows.append(cur)
+            elif cur is not None:
+                cur[key] = val
+        return src, var, rows
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
+        results = list(ex.map(one, jobs))
+    out = ["| source | variant | kernel | VGPRs | AGPRs | SGPRs | scratch B/lane | waves/SIMD | LDS B |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for src, var, rows in results:
+        for r in rows:
+            out.append(f"| {src} | {var or 'shipped'} | `{r['kernel']}` | {r.get('VGPRs')} | {r.get('AGPRs')} | "
+                       f"{r.get('TotalSGPRs')} | {r.get('ScratchSize')} | {r.get('Occupancy')} | {r.get('LDS Size')} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resource-usage" in sys.argv:
+        print(resource_usage(verbose="-v" in sys.argv, sources=[a for a in sys.argv[1:] if a.endswith(".hip")]))
+        sys.exit(0)
+    print(build(verbose="-v" in sys.argv, variants="--no-variants" not in sys.argv))

@@ -44,6 +44,14 @@ int check_shape(int B, int N, int Hq, int Hkv, int d) {
   return TATTN_OK;
 }
 
+// The kernels address a 64-key K/V tile with a 32-bit byte offset per lane on top
+// of a 64-bit tile base: 64 rows of Hkv heads must span less than 4 GiB.
+int check_tile_span(int Hkv, int row_bytes) {
+  if ((long long)Hkv * row_bytes * 64 >= (1LL << 32))
+    return fail(TATTN_ERR_INVALID_ARG, "Hkv = %d: 64 key rows of all KV heads must span < 4 GiB", Hkv);
+  return TATTN_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return TATTN_OK;
   return fail(TATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
@@ -106,6 +114,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (int s = check_shape(B, N, Hq, Hkv, d)) return s;
   if (d != 64 && d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
   if (dtype != TATTN_F16 && dtype != TATTN_BF16) return fail(TATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (int s = check_tile_span(Hkv, 2 * d)) return s;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(TATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (causal != 0 && causal != 1) return fail(TATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -129,6 +138,7 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const 
   if (int s = check_shape(B, N, Hq, Hkv, d)) return s;
   if (d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (fp8 path supports 128)", d);
   if (N > 262144) return fail(TATTN_ERR_UNSUPPORTED, "N = %d > 262144 on the fp8 path", N);
+  if (int s = check_tile_span(Hkv, d)) return s;
   if (out_dtype != TATTN_F16 && out_dtype != TATTN_BF16)
     return fail(TATTN_ERR_UNSUPPORTED, "out_dtype %d", out_dtype);
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))

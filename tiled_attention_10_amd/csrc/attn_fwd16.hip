@@ -59,7 +59,46 @@ constexpr int NW = 8;                // waves per workgroup
 constexpr int kThreads = 64 * NW;
 constexpr int BM = 32 * NW;          // query rows per workgroup
 constexpr int BN = 64;               // keys per tile
-constexpr int STAGES = 4;
+
+// Schedule of the tile loop.  The library ships the default; the other settings
+// build the variants the scheduling ablation compares (selected at build time):
+//   STAGES       ring depth of the K and V rings (>= 3).  During step j the loads
+//                of K(j + STAGES-1) and V(j + STAGES-2) go out while K(j), K(j+1),
+//                V(j-1) and V(j) are read, so three stages is the least this
+//                two-group schedule can run with (each step reads two K tiles).
+//   READ_AHEAD   products between an LDS operand read and the product using it.
+//   PINGPONG     two wave groups alternating exponentials and products (true), or
+//                every wave on the same softmax -> P·V -> scores order (false).
+//   SPLIT_LOADS  a step's tile loads issued at two points of each wave's schedule
+//                (true), or all right after the barrier (false).
+#ifndef TATTN_STAGES
+#define TATTN_STAGES 4
+#endif
+#ifndef TATTN_READ_AHEAD
+#define TATTN_READ_AHEAD 2
+#endif
+#ifndef TATTN_PINGPONG
+#define TATTN_PINGPONG 1
+#endif
+#ifndef TATTN_SPLIT_LOADS
+#define TATTN_SPLIT_LOADS 1
+#endif
+constexpr int STAGES = TATTN_STAGES;
+constexpr int kReadAhead = TATTN_READ_AHEAD;
+constexpr bool kPingPong = TATTN_PINGPONG != 0;
+constexpr bool kSplitLoads = TATTN_SPLIT_LOADS != 0;
+static_assert(STAGES >= 3 && STAGES <= 5, "ring depth");
+constexpr int KDIST = STAGES - 1;    // K(j + KDIST) is loaded during step j
+constexpr int VDIST = STAGES - 2;    // V(j + VDIST) likewise
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1.
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Largest partial row sum of probabilities accepted before the reference max
 // is moved: keeps every probability below the fp16 operand range.
@@ -85,9 +124,6 @@ struct Geo {
     }
   }
 };
-
-// Products between an LDS read and the product that consumes it.
-constexpr int kReadAhead = 2;
 
 struct KernelParams {
   const uint16_t* q;
@@ -126,9 +162,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   const int nsub = (CAUSAL && r != p.nqt - 1 - r) ? 2 : 1;
   for (int sub = 0; sub < nsub; ++sub) {
   const int qt = CAUSAL ? (sub == 0 ? p.nqt - 1 - r : r) : r;
-  // Opaque per item: lane-derived offsets are recomputed for each item instead of
-  // being hoisted out of the item loop and kept live through the tile loop.
-  int lane = tid & 63;
+  // The lane index comes from mbcnt, which needs no live register, and is opaque
+  // per item: lane-derived offsets are recomputed for each item instead of being
+  // hoisted out of the item loop and kept live through the tile loop.
+  int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   asm volatile("" : "+v"(lane));
   const int l32 = lane & 31, hh = lane >> 5;
   const int hq = rest % p.Hq;
@@ -176,7 +213,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     ld_row[n] = r;
     ld_col[n] = 16 * (pc ^ G::swz(r));
   }
-  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  // LDS address of this wave's first 1 KB load slot; the ring and stage offsets are
+  // compile-time constants added to it, and it is opaque so that the compiler does
+  // not keep one scalar register per (ring, stage, load) through the loop.
+  uint32_t lds_wave = (uint32_t)(uintptr_t)lds + 1024 * (wave * LOADS);
+  asm volatile("" : "+s"(lds_wave));
   uint32_t ld_off[LOADS];   // byte offset of this lane's 16 bytes within a tile (same for K and V)
 #pragma unroll
   for (int n = 0; n < LOADS; ++n) ld_off[n] = (uint32_t)(ld_row[n] * kvrow + ld_col[n]);
@@ -197,8 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     const bool last = t == nt - 1;
 #pragma unroll
     for (int n = 0; n < LOADS; ++n)
-      lds_dma16(base, last ? ld_off_last[n] : ld_off[n],
-                lds_base + (ring * STAGES + stage) * G::TILEB + 1024 * (wave * LOADS + n));
+      lds_dma16(base, last ? ld_off_last[n] : ld_off[n], lds_wave + (ring * STAGES + stage) * G::TILEB + 1024 * n);
   };
 
   // Per-lane LDS read offsets within a stage.
@@ -255,15 +295,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   //   group 0: softmax(j)              | P·V(j), scores(j+1)   (scores(0) in the prologue)
   //   group 1: P·V(j-1), scores(j)     | softmax(j)            (P·V(last) after the loop)
   // so each wave's softmax runs while the other wave of its SIMD issues both of
-  // its products.  Step j reads K(j), K(j+1), V(j-1) and V(j).
-  const bool lead = wave < NW / 2;
+  // its products.  Step j reads K(j), K(j+1), V(j-1) and V(j).  Without the
+  // ping-pong every wave runs group 0's order.
+  const bool lead = !kPingPong || wave < NW / 2;
   vec8 pf[BN / 16] = {};   // probabilities of the last softmax (operand of the next P·V)
 
-  // Prologue: K tiles 0..2 and V tiles 0..1, then scores(0) for group 0.
+  // Prologue: K tiles 0 .. KDIST-1 and V tiles 0 .. VDIST-1, then scores(0) for group 0.
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t) {
+  for (int t = 0; t < KDIST; ++t) {
     if (t < nt) issue(0, t, t);
-    if (t < STAGES - 2 && t < nt) issue(1, t, t);
+    if (t < VDIST && t < nt) issue(1, t, t);
   }
   wait_vmcnt<0>();
   barrier();
@@ -303,16 +344,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     constexpr bool lead = decltype(leadc)::value;
     constexpr int stn = (st + 1) % STAGES;
     constexpr int stp = (st + STAGES - 1) % STAGES;
-    // Needed now: K(j+1) and V(j), issued two steps ago.  Allowed in flight: K(j+2)
-    // and V(j+1) from the last step.  The barrier also retires every wave's reads
-    // of K(j-1) and V(j-2), whose stages receive K(j+3) and V(j+2) in this step.
-    wait_vmcnt<2 * LOADS>();
+    // Needed now: K(j+1) and V(j), issued in step j+2-STAGES.  Allowed in flight: the
+    // loads of the STAGES-3 steps since.  The barrier also retires every wave's reads
+    // of K(j-1) and V(j-2), whose stages receive K(j+KDIST) and V(j+VDIST) in this step.
+    wait_vmcnt<(STAGES - 3) * 2 * LOADS>();
     barrier();
     // The tile loads of a step go out at two points of each wave's schedule, which
     // differ between the groups: issued all at once, the loads of eight waves queue
     // in the address unit and stall the issuing waves.
-    auto load_k = [&]() { issue(0, (st + 3) % STAGES, j + 3); };
-    auto load_v = [&]() { issue(1, (st + 2) % STAGES, j + 2); };
+    auto load_k = [&]() { issue(0, (st + KDIST) % STAGES, j + KDIST); };
+    auto load_v = [&]() { issue(1, (st + VDIST) % STAGES, j + VDIST); };
+    if constexpr (!kSplitLoads) {
+      load_k();
+      load_v();
+    }
+    auto load_k_split = [&]() { if constexpr (kSplitLoads) load_k(); };
+    auto load_v_split = [&]() { if constexpr (kSplitLoads) load_v(); };
 
     // Online softmax of tile j ([FA3-V3] §4.2), fp32 statistics.  The row max is
     // only taken on the first tile and when the probabilities of a tile would no
@@ -383,21 +430,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     };
     if constexpr (lead) {
       if (j >= ntw) {
-        load_k();
-        load_v();
+        load_k_split();
+        load_v_split();
         return;
       }
       softmax();
       __builtin_amdgcn_sched_barrier(0);
-      load_k();
+      load_k_split();
       pv_only(st);
-      load_v();
+      load_v_split();
       if (j + 1 < ntw) scores_only(stn);
     } else {
       const bool has_pv = j >= 1 && j - 1 < ntw, has_scores = j < ntw;
-      load_k();
+      load_k_split();
       if (has_pv) pv_only(stp);
-      load_v();
+      load_v_split();
       if (has_scores) scores_only(st);
       if (!has_scores) return;
       __builtin_amdgcn_sched_barrier(0);
@@ -407,15 +454,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   // Separate loops per group keep the two schedules' register lifetimes apart.
   auto run = [&](auto leadc) {
     for (int j = 0; j < nt; j += STAGES) {
-      step(std::integral_constant<int, 0>{}, leadc, j);
-      if (j + 1 < nt) step(std::integral_constant<int, 1>{}, leadc, j + 1);
-      if (j + 2 < nt) step(std::integral_constant<int, 2>{}, leadc, j + 2);
-      if (j + 3 < nt) step(std::integral_constant<int, 3>{}, leadc, j + 3);
+      static_for<0, STAGES>([&](auto stc) {
+        if (decltype(stc)::value == 0 || j + decltype(stc)::value < nt) step(stc, leadc, j + decltype(stc)::value);
+      });
     }
   };
   if (lead) {
     run(std::true_type{});
-  } else {
+  } else if constexpr (kPingPong) {
     run(std::false_type{});
     if (ntw == nt && nt > 0) pv_only((nt - 1) % STAGES);
   }
