@@ -209,6 +209,28 @@ int attn_decode_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_ca
  * function of B, Nmax, Hq, Hkv). */
 size_t attn_decode_fp8kv_workspace_size(int B, int Nmax, int Hq, int Hkv, int d);
 
+/*
+ * attn_decode_fp8kv_noalloc — attn_decode_fp8kv for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  It computes exactly what
+ * attn_decode_fp8kv computes, with the same kernels, arguments (less the
+ * workspace), checks and error codes, and allocates nothing: the chunk
+ * partials go to a fixed scratch array of TATTN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  Sizes whose
+ * attn_decode_fp8kv_workspace_size() exceeds that return
+ * TATTN_ERR_INVALID_ARG.  The first call on a device looks up that device's
+ * address of the array (a failure returns TATTN_ERR_HIP).  Every call on one
+ * GPU uses the same array: calls that overlap in time on one GPU (different
+ * streams, or threads) race and must be serialised by the caller.  Nothing in
+ * the array needs to start at zero; every value the step reads is written by
+ * the same call first.
+ */
+#define TATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_decode_fp8kv_noalloc(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* seqlens,
+                              void* o, float* lse, int B, int Nmax, int Hq, int Hkv, int d,
+                              float softmax_scale, int dtype, void* stream);
+
 /* Text for a status code (static storage). */
 const char* tattn_status_string(int status);
 

@@ -173,3 +173,29 @@ def test_clock_probe_library():
     assert P.tattn_clock_probe(10, 10, None, None) == 1
     out = subprocess.run(["nm", "-D", "--defined-only", T.LIB_PATH], capture_output=True, text=True).stdout
     assert "tattn_clock_probe" not in out
+
+
+def decode_noalloc(L, q=P, kc=P, vc=P, ks=P, vs=P, sl=P, o=P, lse=None, B=2, Nmax=1000, Hq=8, Hkv=2, d=128,
+                   scale=0.1, dtype=2):
+    return L.attn_decode_fp8kv_noalloc(q, kc, vc, ks, vs, sl, o, lse, B, Nmax, Hq, Hkv, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(sl=None), INVALID), (dict(B=0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED), (dict(scale=0.0), INVALID),
+    (dict(q=BAD), MISALIGNED), (dict(ks=P + 2), MISALIGNED),
+    # needs more than the fixed scratch: rejected before any HIP call
+    (dict(B=64, Nmax=131072, Hq=64, Hkv=8), INVALID),
+])
+def test_attn_decode_fp8kv_noalloc_rejects(L, kw, status):
+    assert decode_noalloc(L, **kw) == status
+    assert L.tattn_last_error() != b""
+
+
+def test_noalloc_scratch_limit_against_workspace_sizes(L):
+    limit = 16 << 20
+    assert L.attn_decode_fp8kv_workspace_size(64, 131072, 64, 8, 128) > limit
+    # the benchmark's decode workload fits
+    assert 0 < L.attn_decode_fp8kv_workspace_size(4, 131072, 64, 8, 128) <= limit
+    decode_noalloc(L, B=64, Nmax=131072, Hq=64, Hkv=8)
+    assert b"scratch" in L.tattn_last_error()

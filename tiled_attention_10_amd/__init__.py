@@ -15,12 +15,13 @@ import os
 
 __all__ = ["attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "attn_decode_fp8kv",
            "decode_workspace_size", "TattnError", "lib", "LIB_PATH", "TATTN_F16", "TATTN_BF16",
-           "use_library", "variant_path"]
+           "use_library", "variant_path", "attn_decode_fp8kv_noalloc", "TATTN_NOALLOC_SCRATCH_BYTES"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtattn.so")
 
 TATTN_F16 = 1
 TATTN_BF16 = 2
+TATTN_NOALLOC_SCRATCH_BYTES = 16 << 20     # the fixed decode scratch of attn_decode_fp8kv_noalloc
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "misaligned", 4: "HIP error"}
 
 _lib = None
@@ -82,6 +83,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.attn_decode_fp8kv.restype = i
     L.attn_decode_fp8kv_workspace_size.argtypes = [i, i, i, i, i]
     L.attn_decode_fp8kv_workspace_size.restype = ctypes.c_size_t
+    L.attn_decode_fp8kv_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_decode_fp8kv_noalloc.restype = i
     L.tattn_status_string.argtypes = [i]
     L.tattn_status_string.restype = ctypes.c_char_p
     L.tattn_last_error.argtypes = []
@@ -288,4 +291,38 @@ def attn_decode_fp8kv(q, k_cache, v_cache, k_scale, v_scale, seqlens, softmax_sc
     _check(lib().attn_decode_fp8kv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                    _ptr(seqlens), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
                                    B, Nmax, Hq, Hkv, d, scale, code, _stream(dev)))
+    return (out, lse) if lse is not None else out
+
+
+def attn_decode_fp8kv_noalloc(q, k_cache, v_cache, k_scale, v_scale, seqlens, softmax_scale: float | None = None,
+                              out=None, return_lse: bool = False, lse=None):
+    """``attn_decode_fp8kv`` through the entry point that allocates nothing: the library's
+    fixed per-device scratch (TATTN_NOALLOC_SCRATCH_BYTES) replaces the workspace.  Pass
+    ``out`` (and ``lse``) to keep this call free of allocations as well; calls that overlap
+    in time on one GPU race on the shared scratch."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and the caches [B, Nmax, Hkv, d]")
+    B, Hq, d = q.shape
+    if tuple(k_cache.shape) != tuple(v_cache.shape) or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k_cache.shape)}, v {tuple(v_cache.shape)}")
+    Nmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    for t in (k_cache, v_cache):
+        if t.dtype != torch.uint8:
+            raise TypeError("caches must be uint8 E4M3FN codes")
+    nb = (Nmax + 63) // 64
+    for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, Hkv, nb):
+            raise ValueError(f"{name} must be float32 {(B, Hkv, nb)}")
+    if seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (B,):
+        raise ValueError(f"seqlens must be int32 [{B}]")
+    code = _dtype_code(q.dtype)
+    dev = _dev(q, k_cache, v_cache, k_scale, v_scale, seqlens)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = _out(out, (B, Hq, d), q.dtype, dev, "out")
+    if return_lse or lse is not None:
+        lse = _out(lse, (B, Hq), torch.float32, dev, "lse")
+    _check(lib().attn_decode_fp8kv_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                           _ptr(seqlens), _ptr(out), _ptr(lse), B, Nmax, Hq, Hkv, d, scale, code,
+                                           _stream(dev)))
     return (out, lse) if lse is not None else out

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "tattn.h"
 #include "tattn_launch.hpp"
@@ -71,6 +72,72 @@ int rotate_common(const void* x, void* y, const float* rope_cos, const float* ro
   a.rope_cos = rope_cos; a.rope_sin = rope_sin;
   a.B = B; a.N = N; a.H = H; a.d = d; a.dtype = in_dtype;
   return hip_status(tattn::launch_hadamard_rotate(a, (hipStream_t)stream), "rotation launch");
+}
+
+// Device scratch of attn_decode_fp8kv_noalloc, for callers that cannot allocate:
+// one copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: the per-device address comes from
+// hipGetSymbolAddress on the first call on each device.
+constexpr size_t kNoAllocScratchBytes = TATTN_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+// This device's address of ``scratch`` (looked up once per device), or nullptr with
+// the failure recorded in the last-error string.
+void* noalloc_scratch() {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) {
+    fail(TATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fail(TATTN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+// Checks and launch of one decode step with the given workspace (validated
+// here except for the workspace itself, which the callers check).
+int decode_common(const void* q, const uint8_t* k_cache, const uint8_t* v_cache, const float* k_scale,
+                  const float* v_scale, const int32_t* seqlens, void* o, float* lse, int B, int Nmax, int Hq,
+                  int Hkv, int d, float softmax_scale, int dtype, tattn::DecodePlan* plan) {
+  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !seqlens || !o)
+    return fail(TATTN_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || Nmax < 1 || Hq < 1 || Hkv < 1)
+    return fail(TATTN_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d Nmax=%d Hq=%d Hkv=%d)", B, Nmax, Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(TATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (the decode path supports 128)", d);
+  if (dtype != TATTN_F16 && dtype != TATTN_BF16) return fail(TATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (too_large(B, Nmax, Hq, d) || too_large(B, Nmax, Hkv, d) || Hkv > 65536 || B > 65535)
+    return fail(TATTN_ERR_INVALID_ARG, "sizes too large (B=%d Nmax=%d Hq=%d Hkv=%d)", B, Nmax, Hq, Hkv);
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(TATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+    return fail(TATTN_ERR_MISALIGNED, "q, caches and o must be 16-byte aligned");
+  if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(seqlens, 4) || (lse && !aligned(lse, 4)))
+    return fail(TATTN_ERR_MISALIGNED, "scales, seqlens and lse must be 4-byte aligned");
+  *plan = tattn::plan_decode(B, Nmax, Hq, Hkv);
+  if ((long long)Hkv * plan->nhg > 65535) return fail(TATTN_ERR_INVALID_ARG, "too many head groups");
+  return TATTN_OK;
+}
+
+int decode_launch(const void* q, const uint8_t* k_cache, const uint8_t* v_cache, const float* k_scale,
+                  const float* v_scale, const int32_t* seqlens, void* o, float* lse, void* workspace, int B,
+                  int Nmax, int Hq, int Hkv, int d, float softmax_scale, int dtype, void* stream) {
+  tattn::DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.seqlens = seqlens; a.o = o; a.lse = lse; a.workspace = workspace;
+  a.B = B; a.Nmax = Nmax; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.scale = softmax_scale; a.dtype = dtype;
+  return hip_status(tattn::launch_attn_decode(a, (hipStream_t)stream), "attn_decode_fp8kv launch");
 }
 
 }  // namespace
@@ -184,31 +251,34 @@ int attn_decode_fp8kv(const void* q, const uint8_t* k_cache, const uint8_t* v_ca
                       size_t workspace_bytes, int B, int Nmax, int Hq, int Hkv, int d, float softmax_scale,
                       int dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !seqlens || !o || !workspace)
-    return fail(TATTN_ERR_INVALID_ARG, "null pointer");
-  if (B < 1 || Nmax < 1 || Hq < 1 || Hkv < 1)
-    return fail(TATTN_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d Nmax=%d Hq=%d Hkv=%d)", B, Nmax, Hq, Hkv);
-  if (Hq % Hkv != 0) return fail(TATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-  if (d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (the decode path supports 128)", d);
-  if (dtype != TATTN_F16 && dtype != TATTN_BF16) return fail(TATTN_ERR_UNSUPPORTED, "dtype %d", dtype);
-  if (too_large(B, Nmax, Hq, d) || too_large(B, Nmax, Hkv, d) || Hkv > 65536 || B > 65535)
-    return fail(TATTN_ERR_INVALID_ARG, "sizes too large (B=%d Nmax=%d Hq=%d Hkv=%d)", B, Nmax, Hq, Hkv);
-  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
-    return fail(TATTN_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
-      !aligned(workspace, 16))
-    return fail(TATTN_ERR_MISALIGNED, "q, caches, o and workspace must be 16-byte aligned");
-  if (!aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(seqlens, 4) || (lse && !aligned(lse, 4)))
-    return fail(TATTN_ERR_MISALIGNED, "scales, seqlens and lse must be 4-byte aligned");
-  const tattn::DecodePlan pl = tattn::plan_decode(B, Nmax, Hq, Hkv);
-  if ((long long)Hkv * pl.nhg > 65535) return fail(TATTN_ERR_INVALID_ARG, "too many head groups");
+  tattn::DecodePlan pl{};
+  if (int s = decode_common(q, k_cache, v_cache, k_scale, v_scale, seqlens, o, lse, B, Nmax, Hq, Hkv, d,
+                            softmax_scale, dtype, &pl))
+    return s;
+  if (!workspace) return fail(TATTN_ERR_INVALID_ARG, "null workspace");
+  if (!aligned(workspace, 16)) return fail(TATTN_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   if (workspace_bytes < pl.ws_bytes)
     return fail(TATTN_ERR_INVALID_ARG, "workspace of %zu bytes < %zu required", workspace_bytes, pl.ws_bytes);
-  tattn::DecodeArgs a{};
-  a.q = q; a.k = k_cache; a.v = v_cache; a.k_scale = k_scale; a.v_scale = v_scale;
-  a.seqlens = seqlens; a.o = o; a.lse = lse; a.workspace = workspace;
-  a.B = B; a.Nmax = Nmax; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.scale = softmax_scale; a.dtype = dtype;
-  return hip_status(tattn::launch_attn_decode(a, (hipStream_t)stream), "attn_decode_fp8kv launch");
+  return decode_launch(q, k_cache, v_cache, k_scale, v_scale, seqlens, o, lse, workspace, B, Nmax, Hq, Hkv, d,
+                       softmax_scale, dtype, stream);
+}
+
+int attn_decode_fp8kv_noalloc(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* seqlens, void* o,
+                              float* lse, int B, int Nmax, int Hq, int Hkv, int d, float softmax_scale,
+                              int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  tattn::DecodePlan pl{};
+  if (int s = decode_common(q, k_cache, v_cache, k_scale, v_scale, seqlens, o, lse, B, Nmax, Hq, Hkv, d,
+                            softmax_scale, dtype, &pl))
+    return s;
+  if (pl.ws_bytes > kNoAllocScratchBytes)
+    return fail(TATTN_ERR_INVALID_ARG, "these sizes need %zu bytes of decode scratch; the fixed scratch holds %zu",
+                pl.ws_bytes, kNoAllocScratchBytes);
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return TATTN_ERR_HIP;
+  return decode_launch(q, k_cache, v_cache, k_scale, v_scale, seqlens, o, lse, ws, B, Nmax, Hq, Hkv, d,
+                       softmax_scale, dtype, stream);
 }
 
 }  // extern "C"
