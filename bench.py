@@ -12,7 +12,8 @@ With --dtype fp8 a step is attn_fwd_fp8 on E4M3 codes prepared once by
 hadamard_rotate (rotation + quantisation, timed separately as the prologue).
 
 Prints ONE JSON line: throughput in TFLOPS (4·N²·d·Hq·B per step, halved when
-causal; mean over the timed steps, plus per-launch median and min), the
+causal; mean over the timed steps, plus per-launch median and min; the other GPU
+legs below run before the timed steps, so that the GPU's clocks have settled), the
 attention kernel's roofline against the dense matrix-core peak (and against that peak
 scaled to the shader clock a one-wave probe on a second stream measures under the same load),
 its HBM traffic when a counter measurement of the current kernel source is on
@@ -128,10 +129,18 @@ def cpu_baseline(q, k, v, causal, rows_per_head, seed):
                       f"{flops:.3e} flop in {dt:.2f} s"}
 
 
-def time_launches(torch, fn, steps, warmup, stream):
+def time_launches(torch, fn, steps, warmup, stream, min_warm_s=0.0):
+    """Mean ms per launch over ``steps`` launches after ``warmup`` untimed ones (and, with
+    ``min_warm_s``, more untimed launches until that much wall time has passed, so that a
+    short kernel is timed at the clocks a sustained run settles to)."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
@@ -221,19 +230,20 @@ def measured_clock_ghz(torch, fn, dev, launches=20):
     return round(cycles / ticks * 0.1, 3) if ticks > 0 else None
 
 
-def fp8_rmse_leg(T, torch, W, dev, nrows=256):
+def fp8_rmse_leg(T, torch, W, dev, nrows=None):
     """Output RMSE of the fp8 path against exact attention of the unquantised 16-bit inputs,
     with and without the random-sign Hadamard rotation of Q and K, on the outlier workload
     (one x20 channel per head).  Q, K, V are quantised by the GPU prologue and attended by the
-    fp8 kernel; the reference is the fp64 CPU oracle on ``nrows`` seeded query rows per
-    (batch, head), computed on the host after every timed region."""
+    fp8 kernel; the reference is the fp64 CPU oracle on every query row (or ``nrows`` seeded
+    rows) of every (batch, head), computed on the host after every timed region."""
     import numpy as np
     from oracle import attention as A
 
     w = W.WORKLOADS["fp8_outlier_b2_h16_n4096"]
     qh, kh, vh = (W.to_torch(x, "bf16") for x in W.qkv_f32(w))
     q, k, v = qh.to(dev), kh.to(dev), vh.to(dev)
-    rows = np.sort(np.random.default_rng(w.wid).choice(w.N, nrows, replace=False))
+    rows = (np.arange(w.N) if nrows is None
+            else np.sort(np.random.default_rng(w.wid).choice(w.N, nrows, replace=False)))
     signs = torch.from_numpy(W.rotation_signs(w.wid, w.d)).to(dev)
     outs = {}
     for rot in (False, True):
@@ -249,7 +259,8 @@ def fp8_rmse_leg(T, torch, W, dev, nrows=256):
     for rot in (False, True):
         res["with_hadamard" if rot else "without_hadamard"] = round(float(np.sqrt(np.mean((outs[rot] - ref) ** 2))), 6)
     res["ratio_without_over_with"] = round(res["without_hadamard"] / res["with_hadamard"], 3)
-    res["sample"] = (f"{w.name}: {nrows} seeded query rows x {w.Hq} heads x B={w.B}; reference: the fp64 "
+    which = f"all {w.N}" if nrows is None else f"{nrows} seeded"
+    res["sample"] = (f"{w.name}: {which} query rows x {w.Hq} heads x B={w.B}; reference: the fp64 "
                      f"CPU oracle (oracle.attention.attention_rows) on the bf16 inputs, {dt:.1f} s on the host")
     return res
 
@@ -300,14 +311,14 @@ def _cores():
         return os.cpu_count()
 
 
-def decode_bench(T, torch, W, name, steps, warmup, stream, dev, cpu=True):
+def decode_bench(T, torch, W, name, steps, warmup, stream, dev, cpu=True, min_warm_s=0.0):
     """Time one decode step (split + merge kernels) on a decode workload; HBM roofline."""
     w = W.DECODE_WORKLOADS[name]
     q, kc, vc, ks, vs, sl, seqlens = decode_inputs(T, torch, W, w, dev)
     out = torch.empty_like(q)
     ws = torch.empty(T.decode_workspace_size(w.B, w.Nmax, w.Hq, w.Hkv, w.d), dtype=torch.uint8, device=dev)
     fn = lambda: T.attn_decode_fp8kv(q, kc, vc, ks, vs, sl, out=out, workspace=ws)
-    ms, wall = time_launches(torch, fn, steps, warmup, stream)
+    ms, wall = time_launches(torch, fn, steps, warmup, stream, min_warm_s)
     med, mn = launch_stats(torch, fn, steps, stream)
     nbytes = w.hbm_bytes(seqlens)
     gbps = nbytes / (ms * 1e-3) / 1e9
@@ -329,13 +340,14 @@ def _tf(flops, ms):
     return round(flops / (ms * 1e-3) / 1e12, 2)
 
 
-def config_legs(T, torch, W, stream, dev, steps=10, warmup=10):
+def config_legs(T, torch, W, stream, dev, steps=20, warmup=10, min_warm_s=0.25):
     """Each remaining workload of the method's configurations timed once (inputs resident
-    in HBM): ms per launch (mean over ``steps`` after ``warmup``), TFLOPS, fraction of peak."""
+    in HBM): ms per launch (mean over ``steps`` after at least ``warmup`` launches and
+    ``min_warm_s`` seconds of them), TFLOPS, fraction of peak."""
     out = {}
 
     def leg(name, fn, flops, peak_key, **kw):
-        ms, _ = time_launches(torch, fn, steps, warmup, stream)
+        ms, _ = time_launches(torch, fn, steps, warmup, stream, min_warm_s)
         out[name] = {"ms": round(ms, 4), "tflops": _tf(flops, ms),
                      "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[peak_key], 4), **kw}
         print(f"[bench] config {name}: {ms:.4f} ms", file=sys.stderr, flush=True)
@@ -378,27 +390,32 @@ def ablation(args, T, torch, W, stream, dev):
     """The workload timed with the shipped library and each scheduling variant, in
     interleaved rounds (shipped, v1, v2, ..., shipped, v1, ...), median over rounds."""
     import statistics
-    from tiled_attention_10_amd.build import VARIANTS
+    from tiled_attention_10_amd.build import FP8_VARIANTS, VARIANTS
 
     w = W.WORKLOADS[args.workload]
     causal = bool(args.causal)
     dt = "bf16" if args.dtype == "fp8" else args.dtype
     q, k, v = (W.to_torch(x, dt).to(dev) for x in W.qkv_f32(w))
     o = torch.empty_like(q)
-    names = ["shipped"] + sorted(VARIANTS)
+    if args.dtype == "fp8":
+        ins, _, _ = fp8_inputs(T, torch, W, w, q, k, v, dev)
+        names = ["shipped"] + sorted(FP8_VARIANTS)
+        step = lambda: T.attn_fwd_fp8(*ins, causal=causal, out=o)
+    else:
+        names = ["shipped"] + sorted(VARIANTS)
+        step = lambda: T.attn_fwd(q, k, v, causal=causal, out=o)
     times = {n: [] for n in names}
     for r in range(args.rounds):
         for n in names:
             path = T.LIB_PATH if n == "shipped" else T.variant_path(n)
             with T.use_library(path):
-                ms, _ = time_launches(torch, lambda: T.attn_fwd(q, k, v, causal=causal, out=o), args.steps,
-                                      args.warmup, stream)
+                ms, _ = time_launches(torch, step, args.steps, args.warmup, stream)
             times[n].append(ms)
             print(f"[ablation] round {r} {n}: {ms:.4f} ms", file=sys.stderr, flush=True)
     flops = w.flops(causal)
     base = statistics.median(times["shipped"])
     res = {"metric": "attention fwd TFLOPS per scheduling variant (4·N²·d·H, causal/2)", "unit": "TFLOPS",
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "rounds": args.rounds, "dtype": dt,
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "rounds": args.rounds, "dtype": args.dtype,
            "config": {"workload": w.name + ("_causal" if causal else "_noncausal"), "B": w.B, "N": w.N,
                       "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": causal},
            "variants": {}}
@@ -465,6 +482,32 @@ def main():
     flops = w.flops(causal)
     wl_name = w.name + ("_causal" if causal else "_noncausal")
 
+    # The other GPU legs run first, back to back, so that the step below is timed on a
+    # GPU whose clocks have settled (after an idle period they ramp up over the first
+    # ~20 launches); the legs that only use the host run last.
+    pre = {}
+    fp8_leg = args.dtype != "fp8" and not args.no_fp8 and w.d == 128
+    if fp8_leg:
+        ins8, prologue8, prologue_rope = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
+        out8 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
+        fms, _ = time_launches(torch, lambda: T.attn_fwd_fp8(*ins8, causal=causal, out=out8),
+                               args.steps, args.warmup, stream, min_warm_s=0.25)
+        pms, _ = time_launches(torch, prologue8, 20, 10, stream, min_warm_s=0.1)
+        prms, _ = time_launches(torch, prologue_rope[0], 20, 10, stream, min_warm_s=0.1)
+        purms, _ = time_launches(torch, prologue_rope[1], 20, 10, stream, min_warm_s=0.1)
+        pbytes = prologue_bytes(qd, kd, vd)
+        pre["fp8_prologue"] = {"ms": round(pms, 4), "with_rope_ms": round(prms, 4),
+                               "with_rope_separate_pass_ms": round(purms, 4),
+                               "hbm_bytes": pbytes, "GB_per_s": round(pbytes / (pms * 1e-3) / 1e9, 1),
+                               "with_rope_GB_per_s": round(pbytes / (prms * 1e-3) / 1e9, 1),
+                               "frac_of_hbm_8TBps": round(pbytes / (pms * 1e-3) / 8e12, 4)}
+        del out8
+    if not args.no_configs:
+        pre["configs"] = config_legs(T, torch, W, stream, dev)
+    if not args.no_decode:
+        pre["decode"] = decode_bench(T, torch, W, "decode_fp8kv_b4_h64kv8_n131072", args.steps, args.warmup,
+                                     stream, dev, cpu=False, min_warm_s=0.25)
+
     extra = {}
     if args.dtype == "fp8":
         ins, prologue, _ = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
@@ -507,29 +550,16 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     res.update(extra)
-    if args.dtype != "fp8" and not args.no_fp8 and w.d == 128:
-        ins, prologue, prologue_rope = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
-        out8 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
-        fms, _ = time_launches(torch, lambda: T.attn_fwd_fp8(*ins, causal=causal, out=out8),
-                               args.steps, args.warmup, stream)
-        pms, _ = time_launches(torch, prologue, 20, 10, stream)
-        prms, _ = time_launches(torch, prologue_rope[0], 20, 10, stream)
-        purms, _ = time_launches(torch, prologue_rope[1], 20, 10, stream)
-        pbytes = prologue_bytes(qd, kd, vd)
-        res["fp8_prologue"] = {"ms": round(pms, 4), "with_rope_ms": round(prms, 4),
-                               "with_rope_separate_pass_ms": round(purms, 4),
-                               "hbm_bytes": pbytes, "GB_per_s": round(pbytes / (pms * 1e-3) / 1e9, 1),
-                               "with_rope_GB_per_s": round(pbytes / (prms * 1e-3) / 1e9, 1),
-                               "frac_of_hbm_8TBps": round(pbytes / (pms * 1e-3) / 8e12, 4)}
+    if fp8_leg:
+        res["fp8_prologue"] = pre["fp8_prologue"]
+        pms = pre["fp8_prologue"]["ms"]
         res["fp8"] = {"ms_per_step": round(fms, 4), "tflops": round(flops / (fms * 1e-3) / 1e12, 2),
                       "frac_of_fp8_peak": round(flops / (fms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
                       "prologue_ms": round(pms, 4), "speedup_vs_" + args.dtype: round(ms / fms, 3),
                       "speedup_incl_prologue": round(ms / (fms + pms), 3)}
-    if not args.no_configs:
-        res["configs"] = config_legs(T, torch, W, stream, dev)
-    if not args.no_decode:
-        res["decode"] = decode_bench(T, torch, W, "decode_fp8kv_b4_h64kv8_n131072", args.steps, args.warmup,
-                                     stream, dev, cpu=False)
+    for key in ("configs", "decode"):
+        if key in pre:
+            res[key] = pre[key]
     if args.dtype != "fp8" and not args.no_fp8:
         res["fp8_rmse"] = fp8_rmse_leg(T, torch, W, dev)
     if not args.no_cpu_baseline:

@@ -306,3 +306,23 @@ def test_fp8_equals_exact_attention_when_nothing_rounds(shape, causal):
               for b, r, h, c in bad[:8]]
     assert len(bad) == 0, f"{len(bad)} elements off, max err {err.max():.3g}; (row, head, ch, got, want): {detail}"
     np.testing.assert_allclose(lse[:, :, rows], want_lse, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("variant", sorted(__import__("tiled_attention_10_amd.build", fromlist=["x"]).FP8_VARIANTS))
+def test_fp8_variant_within_derived_bound(variant):
+    # The fp8 variants that compute part of each full tile's exponentials on the VALU
+    # (exp2_valu, relative error <= 1.05e-4, inside the bound's 1e-3 slack): same
+    # derived bound and RMSE check as the shipped kernel, causal (tiles with masked keys
+    # use v_exp_f32 only) and not, with a ragged tail.
+    B, N, Hq, Hkv = 1, 1000, 8, 2
+    q, k, v = (W.to_torch(x, "bf16") for x in W.random_qkv(77, B, N, Hq, Hkv, 128))
+    q8, k8, v8, sq, sk, sv = quantise_all(q, k, v, None)
+    with T.use_library(T.variant_path(variant)):
+        for causal in (False, True):
+            o, lse = run_fp8(q8, k8, v8, sq, sk, sv, causal, lse=True)
+            exact = A.attention(q, k, v, None, causal)
+            emul = fp8_attention_emul(q8, k8, v8, sq, sk, sv, None, causal)
+            e_gpu, e_emul = rmse(o, exact), rmse(emul, exact)
+            print(f"{variant} causal={causal}: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
+            assert np.isfinite(o).all() and e_gpu <= rmse_bound(e_emul)
+            check_derived(o, (q8, k8, v8, sq, sk, sv), causal, lse=lse)

@@ -27,7 +27,8 @@ SOURCES = ["attn_fwd16.hip", "attn_fwd_fp8.hip", "attn_decode.hip", "hadamard.hi
 # Scheduling variants of the 16-bit kernel for the ablation: each is the whole
 # library with attn_fwd16.hip rebuilt under other schedule settings, written to
 # libtattn_<name>.so.  The shipped library uses the defaults in attn_fwd16.hip
-# (4-stage rings, reads 2 products ahead, two-group ping-pong, split loads).
+# (4-stage rings, reads 2 products ahead, two-group ping-pong, split loads,
+# scale applied in fp32).
 VARIANTS = {
     "stages3": ["-DTATTN_STAGES=3"],
     "stages5": ["-DTATTN_STAGES=5"],
@@ -35,6 +36,17 @@ VARIANTS = {
     "readahead1": ["-DTATTN_READ_AHEAD=1"],
     "readahead4": ["-DTATTN_READ_AHEAD=4"],
     "loads_at_barrier": ["-DTATTN_SPLIT_LOADS=0"],
+    "foldscale": ["-DTATTN_FOLD_SCALE=1"],
+}
+# Variants whose arithmetic differs from the shipped build (not bit-identical to it).
+ARITH_VARIANTS = {"foldscale"}
+# Variants of the fp8 kernel (attn_fwd_fp8.hip rebuilt, libtattn_<name>.so): part of
+# every 8 exponentials of a full tile on the VALU pipe (exp2_valu) instead of
+# v_exp_f32.  The shipped library computes all of them with v_exp_f32.
+FP8_VARIANTS = {
+    "fp8_expvalu1": ["-DTATTN_FP8_EXP_VALU=1"],
+    "fp8_expvalu2": ["-DTATTN_FP8_EXP_VALU=2"],
+    "fp8_expvalu4": ["-DTATTN_FP8_EXP_VALU=4"],
 }
 
 
@@ -47,7 +59,7 @@ def _compile(src: str, verbose: bool, variant: str | None = None) -> str:
     stem = os.path.splitext(src)[0] + ("" if variant is None else "_" + variant)
     obj = os.path.join(OBJDIR, stem + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    extra = [] if variant is None else VARIANTS[variant]
+    extra = [] if variant is None else {**VARIANTS, **FP8_VARIANTS}[variant]
     cmd = [_hipcc(), *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -93,29 +105,33 @@ def build(verbose: bool = False, variants: bool = True) -> str:
     (unless ``variants`` is False) and the benchmark's clock probe; returns the
     library's path."""
     os.makedirs(OBJDIR, exist_ok=True)
-    jobs = [(s, None) for s in SOURCES] + ([("attn_fwd16.hip", v) for v in VARIANTS] if variants else [])
+    var_jobs = ([("attn_fwd16.hip", v) for v in VARIANTS] + [("attn_fwd_fp8.hip", v) for v in FP8_VARIANTS]
+                if variants else [])
+    jobs = [(s, None) for s in SOURCES] + var_jobs
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
     base = objs[:len(SOURCES)]
     _link(base, LIB, verbose)
-    for i, v in enumerate(VARIANTS if variants else []):
-        _link([objs[len(SOURCES) + i]] + base[1:], variant_lib(v), verbose)
+    for (src, v), obj in zip(var_jobs, objs[len(SOURCES):]):
+        i = SOURCES.index(src)
+        _link(base[:i] + [obj] + base[i + 1:], variant_lib(v), verbose)
     build_probe(verbose)
     return LIB
 
 
 def resource_usage(verbose: bool = False, sources=None) -> str:
     """Per-kernel register, scratch, occupancy and LDS use of the given sources (default
-    all) and, with attn_fwd16.hip, its scheduling variants, from the compiler's
-    kernel-resource-usage remarks (a markdown table)."""
+    all) and the variants of attn_fwd16.hip and attn_fwd_fp8.hip among them, from the
+    compiler's kernel-resource-usage remarks (a markdown table)."""
     import re
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = [s for s in SOURCES if s.endswith(".hip") and (not sources or s in sources)]
-    jobs = [(s, None) for s in srcs] + ([("attn_fwd16.hip", v) for v in VARIANTS] if "attn_fwd16.hip" in srcs else [])
+    jobs = ([(s, None) for s in srcs] + ([("attn_fwd16.hip", v) for v in VARIANTS] if "attn_fwd16.hip" in srcs else [])
+            + ([("attn_fwd_fp8.hip", v) for v in FP8_VARIANTS] if "attn_fwd_fp8.hip" in srcs else []))
 
     def one(job):
         src, var = job
-        extra = [] if var is None else VARIANTS[var]
+        extra = [] if var is None else {**VARIANTS, **FP8_VARIANTS}[var]
         cmd = [_hipcc(), *FLAGS, *extra, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
                "-o", os.path.join(OBJDIR, "resource_usage_tmp_" + (var or "") + os.path.splitext(src)[0] + ".o")]
         if verbose:

@@ -23,13 +23,19 @@
 //
 // Per tile and wave, on the 32x32x16 matrix cores:
 //   Sᵀ = K·Qᵀ   A = K rows from LDS (rows taken in an order that swaps bits 2
-//                and 3 of the row index), B = c·Q with c = scale·log2(e), so
-//                scores come out in log2 units.  The accumulator starts from
-//                −m_ref, the row's reference max.  Lane l then holds 32 scores
-//                of query row l%32: row statistics are lane-local apart from
-//                one exchange with lane l^32.
-//   softmax     online, fp32 ([FA3-V3] §4.2): p = 2^(accumulator), one v_exp
-//                per element, z' = z + Σp.  The reference max is set on the first
+//                and 3 of the row index), B = Q as given; the accumulator
+//                starts from zero.  Lane l then holds 32 scores of query row
+//                l%32: row statistics are lane-local apart from one exchange
+//                with lane l^32.
+//   softmax     online, fp32 ([FA3-V3] §4.2): p = 2^(c·s − m_ref) with
+//                c = scale·log2(e) and m_ref the row's reference max in log2
+//                units, one fused multiply-add and one v_exp per element,
+//                z' = z + Σp.  (Folding c into Q, rounded to the input type,
+//                and starting the accumulator from −m_ref would save the
+//                multiply-add, but that rounding moves every score of a row
+//                by up to u·scale·Σ|q_i k_i|, an error the method does not
+//                have; it is kept only as a build-time variant.)  The
+//                reference max is set on the first
 //                tile and only moves (by δ, with O and z scaled by 2^−δ) when a
 //                tile's probabilities would leave the 16-bit operand range,
 //                which skips the row max and the O rescale on almost every tile;
@@ -71,6 +77,10 @@ constexpr int BN = 64;               // keys per tile
 //                every wave on the same softmax -> P·V -> scores order (false).
 //   SPLIT_LOADS  a step's tile loads issued at two points of each wave's schedule
 //                (true), or all right after the barrier (false).
+//   FOLD_SCALE   c = scale·log2(e) folded into Q and rounded to the input type, the
+//                score products started from −m_ref, so a probability needs only
+//                the v_exp (true), or Q kept as given and c·s − m_ref formed in
+//                fp32 (false).  Not bit-identical to the shipped build.
 #ifndef TATTN_STAGES
 #define TATTN_STAGES 4
 #endif
@@ -83,10 +93,14 @@ constexpr int BN = 64;               // keys per tile
 #ifndef TATTN_SPLIT_LOADS
 #define TATTN_SPLIT_LOADS 1
 #endif
+#ifndef TATTN_FOLD_SCALE
+#define TATTN_FOLD_SCALE 0
+#endif
 constexpr int STAGES = TATTN_STAGES;
 constexpr int kReadAhead = TATTN_READ_AHEAD;
 constexpr bool kPingPong = TATTN_PINGPONG != 0;
 constexpr bool kSplitLoads = TATTN_SPLIT_LOADS != 0;
+constexpr bool kFoldScale = TATTN_FOLD_SCALE != 0;
 static_assert(STAGES >= 3 && STAGES <= 5, "ring depth");
 constexpr int KDIST = STAGES - 1;    // K(j + KDIST) is loaded during step j
 constexpr int VDIST = STAGES - 2;    // V(j + VDIST) likewise
@@ -183,20 +197,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + l32;
 
-  // Q fragments (B operand of the score MFMA): lane holds c·Q[qrow][16t+8hh .. +7],
-  // c = scale·log2(e), rounded to the input type, so that scores come out in log2 units.
+  // Q fragments (B operand of the score MFMA): lane holds Q[qrow][16t+8hh .. +7]
+  // (folding the scale: c·Q rounded to the input type).
   vec8 qf[D / 16];
   {
     const uint16_t* qr = qb + (long long)min(qrow, N - 1) * qs + 8 * hh;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
       const vec8 raw = __builtin_bit_cast(vec8, *(const u32x4*)(qr + 16 * t));
-      float x[8];
+      if constexpr (kFoldScale) {
+        float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (float)raw[e] * p.c;
-      qf[t] = T::pack8(x);
+        for (int e = 0; e < 8; ++e) x[e] = (float)raw[e] * p.c;
+        qf[t] = T::pack8(x);
+      } else {
+        qf[t] = raw;
+      }
     }
   }
+  const float c = p.c;
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;                    // tiles of the workgroup
@@ -267,20 +286,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
   }
 
   // Defined per item: left undefined, they would be carried from the last item.
-  f32x16 scur[2] = {f32x16{}, f32x16{}};   // scores of the tile whose softmax comes next, minus m_ref
+  f32x16 scur[2] = {f32x16{}, f32x16{}};   // scores of the tile whose softmax comes next
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-  // Reference max of the row (log2 units) and its negation in every element of an
-  // accumulator: the score products start from it, so a score arrives as s - m_ref.
+  // Reference max of the row (log2 units).  Folding the scale, its negation also
+  // fills every element of ``negm``, the start value of the score products, so that
+  // a score arrives as c·s − m_ref; otherwise the products start from zero.
   float m_ref = 0.f, l_run = 0.f;
   f32x16 negm = {};
 
   // Score product S^T = K·Q^T of one K stage into s[2] (keys 0..31 and 32..63).
   auto scores = [&](const int stage, f32x16 (&s)[2]) {
     const lds_char* ks = lds + stage * G::TILEB;
-    s[0] = negm;
-    s[1] = negm;
+    if constexpr (kFoldScale) {
+      s[0] = negm;
+      s[1] = negm;
+    } else {
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+    }
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
 #pragma unroll
@@ -367,15 +392,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
     // score grew more than 15 in log2 units past the reference max).  Between
     // those events the reference max stays put; O/z is the same in exact
     // arithmetic.  The denominator sums the rounded probabilities that enter P·V.
-    // ``shift`` is zero except right after the reference max moved.
+    // Folding the scale, ``shift`` (zero except right after the reference max
+    // moved) is what the accumulators' start value lags behind m_ref.
     auto exps = [&](auto shifted, float shift) {
       float pe[32];
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if constexpr (decltype(shifted)::value) pe[16 * kq + i] = fast_exp2(scur[kq][i] - shift);
-          else pe[16 * kq + i] = fast_exp2(scur[kq][i]);
+          float x;
+          if constexpr (!kFoldScale) x = fmaf(scur[kq][i], c, -m_ref);
+          else if constexpr (decltype(shifted)::value) x = scur[kq][i] - shift;
+          else x = scur[kq][i];
+          pe[16 * kq + i] = fast_exp2(x);
         }
 #pragma unroll
       for (int s = 0; s < BN / 16; ++s) pf[s] = T::pack8(&pe[8 * s]);
@@ -396,7 +425,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
       mt = max_xor32(mt);
-      const float shift = (mt == -INFINITY) ? 0.f : mt;
+      // Folding the scale, mt is the tile's row max of c·s − m_ref, else of s.
+      const float shift = (mt == -INFINITY) ? 0.f : (kFoldScale ? mt : mt * c - m_ref);
       m_ref += shift;
       if (!first) {
         const float alpha = fast_exp2(-shift);
@@ -406,8 +436,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd16_kernel(KernelParams p)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
       }
+      if constexpr (kFoldScale) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) negm[i] = -m_ref;
+        for (int i = 0; i < 16; ++i) negm[i] = -m_ref;
+      }
       return shift;
     };
     auto softmax = [&]() {

@@ -45,6 +45,14 @@ constexpr float kHeadroomLog2 = 8.0f;
 constexpr float kMaxSlack = 0.8f;
 constexpr int kMaxBlocks = 4096;         // scale blocks per head staged in LDS (N <= 262144)
 constexpr int kReadAhead = 2;            // products between an LDS read and its use
+// Of every 8 probabilities of a full tile, how many are computed on the ordinary
+// VALU pipe (exp2_valu) instead of by v_exp_f32, so that the two pipes share the
+// exponentials; tiles with masked keys use v_exp_f32 only.
+#ifndef TATTN_FP8_EXP_VALU
+#define TATTN_FP8_EXP_VALU 0
+#endif
+constexpr int kExpValu = TATTN_FP8_EXP_VALU;
+static_assert(kExpValu >= 0 && kExpValu <= 8, "probabilities per 8 on the VALU");
 
 // Physical 16-byte chunk = logical chunk ^ swz(row) (rows of 128 bytes).
 __device__ inline int swz(int r) {
@@ -284,7 +292,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
     auto softmax = [&]() {
       const int j0 = j * BN;
       const float cj = cj_next, bias = bias_next;
-      if ((j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0)) {
+      const bool edge = (j0 + BN > N) || (CAUSAL && j0 + BN - 1 > wq0);
+      if (edge) {
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
@@ -294,11 +303,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
           }
       }
       l_run = fmaf(tsum[0], tfac, l_run);   // the previous tile's sum, before any rescale
-      float mt = scur[0][0];
+      float mt = max3f(scur[0][0], scur[0][1], scur[0][2]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[0][i]);
+      for (int i = 3; i < 15; i += 2) mt = max3f(mt, scur[0][i], scur[0][i + 1]);
+      mt = max3f(mt, scur[0][15], scur[1][0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, scur[1][i]);
+      for (int i = 1; i < 16; i += 2) mt = max3f(mt, scur[1][i], scur[1][i + 1 < 16 ? i + 1 : i]);
       mt = max_xor32(mt);
       const float m_cand = mt * cj;
       if (__builtin_amdgcn_ballot_w64(m_cand > m_run + kMaxSlack) != 0) {
@@ -312,17 +322,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Fp8Params p) 
           for (int i = 0; i < 16; ++i) oacc[vq][i] *= alpha;
       }
       const float neg = bias - ((m_run == -INFINITY) ? 0.f : m_run);
-      float pe[32];
+      auto exps = [&](auto valu) {
+        constexpr int kv = decltype(valu)::value;
+        float pe[32];
 #pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
+        for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pe[16 * kq + i] = fast_exp2(fmaf(scur[kq][i], cj, neg));
+          for (int i = 0; i < 16; ++i) {
+            const float x = fmaf(scur[kq][i], cj, neg);
+            pe[16 * kq + i] = (i & 7) >= 8 - kv ? exp2_valu(x) : fast_exp2(x);
+          }
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        // (the old-value operand is overwritten byte for byte; passing a source spares a move)
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], __builtin_bit_cast(int, pe[4 * w]), false);
-        pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w + 2], pe[4 * w + 3], word, true);
-      }
+        for (int w = 0; w < 8; ++w) {
+          // (the old-value operand is overwritten byte for byte; passing a source spares a move)
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], __builtin_bit_cast(int, pe[4 * w]), false);
+          pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w + 2], pe[4 * w + 3], word, true);
+        }
+      };
+      if (kExpValu == 0 || edge) exps(std::integral_constant<int, 0>{});
+      else exps(std::integral_constant<int, kExpValu>{});
       // Row sum of this tile's P̃: ones(32x64) · P̃ᵀ puts it in every element of the lane.
       tsum = mfma_fp8(ones, pf, f32x16{});
       tfac = fast_exp2(-bias);

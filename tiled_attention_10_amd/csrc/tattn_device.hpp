@@ -93,8 +93,39 @@ __device__ inline uint32_t pack2(float a, float b) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x on the ordinary VALU pipe, for finite x: the split x = n + f with
+// n = floor(x) and f = fract(x) in [0, 1) (Cody and Waite's range reduction),
+// 2^f from the cubic 1 + f·(a1 + f·(a2 + f·a3)), and the result 2^n·P(f) by
+// v_ldexp.  a1..a3 minimise the largest relative error of P(f)/2^f on [0, 1]
+// under P(0) = 1 and P(1) = 2 (a linear program on a dense grid, see
+// exp2_poly.py): 1.04e-4 evaluated in fp32.  The constraints make the result
+// exact wherever x is an integer and continuous across integers.  A kernel
+// evaluates part of its exponentials this way so that they run beside the
+// v_exp_f32 of the others, which the transcendental unit issues at a fraction
+// of the VALU rate.  Results below 2^-149 flush to zero and large x overflow to
+// +inf, as for v_exp_f32; x = ±inf or NaN is not allowed.
+constexpr float kExp2A1 = 0x1.640ea8p-1f;
+constexpr float kExp2A2 = 0x1.cf7a66p-3f;
+constexpr float kExp2A3 = 0x1.4095eap-4f;
+__device__ inline float exp2_valu(float x) {
+  const float f = __builtin_amdgcn_fractf(x);
+  int n;   // floor(x) as an integer in one instruction (saturates for huge |x|)
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(n) : "v"(x));
+  const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(kExp2A3, f, kExp2A2), f, kExp2A1), f, 1.0f);
+  return __builtin_amdgcn_ldexpf(p, n);
+}
+
 // Exchange with the lane 32 positions away (the other half of the wave).
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max(a, b, c) in one v_max3_f32.  (fmaxf would first quiet signalling NaNs
+// with an extra v_max of each operand with itself; the scores this serves are
+// matrix-core results or -inf, never signalling NaNs.)
+__device__ inline float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // max(x, x of lane ^ 32) without an LDS round trip: v_permlane32_swap exchanges the
 // upper half of one register with the lower half of the other, leaving the lower
@@ -104,7 +135,7 @@ __device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
 __device__ inline float max_xor32(float x) {
   float lo = x, hi = x;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
-  return __builtin_fmaxf(lo, hi);
+  return max3f(lo, hi, hi);
 }
 
 }  // namespace tattn
