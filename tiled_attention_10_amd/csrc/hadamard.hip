@@ -2,18 +2,21 @@
 // for gfx950.  Memory-bound: every element is read once and written once.
 //
 // One workgroup (4 waves) owns one (batch, head, block of 64 rows).  A row of
-// d channels is spread over 4 neighbouring lanes with d/4 consecutive channels
-// each (64 or 32 bytes per lane: coalesced 16-byte loads).  The Walsh–Hadamard
-// butterflies with partner distance 1 .. d/8 run inside a lane; the last two
-// (d/4, d/2) pair lanes 1 and 2 apart, exchanged with DPP quad permutes in the
-// VALU rather than through LDS.  Stages run in increasing distance with one fp32
-// add or subtract each, then one fp32 multiply by fl32(1/sqrt(d)), so the
-// result is fully determined.
+// d channels is spread over 4 neighbouring lanes, in 16-byte chunks of 8
+// channels dealt round-robin: lane l of the quad holds chunks l, l+4, l+8, ...
+// (channel 32v + 8l + e in its element 8v + e), so each 16-byte load of the
+// quad reads 64 contiguous bytes of the row.  The Walsh–Hadamard transform is a
+// product of one butterfly stage per channel-index bit, in any order: the
+// stages over channel bits 0-2 and 5-6 (element distances 1, 2, 4, 8, 16) run
+// inside a lane, and those over bits 3 and 4 (distances 8 and 16) pair lanes 1
+// and 2 apart, exchanged with DPP quad permutes in the VALU rather than through
+// LDS.  Each stage is one fp32 add or subtract per element, followed by one
+// fp32 multiply by fl32(1/sqrt(d)), so the result is fully determined.
 //
 // Rotary embedding (optional, before everything else; [FA3-card] "低精度优化"
 // names it as fusable with the rotation): the partner of channel i is i ± d/2,
-// which sits in the lane two places away in the same quad (d/4 channels per
-// lane), so one more DPP exchange and two fp32 products per element suffice.
+// the top channel-index bit, which this layout keeps inside the lane, so the
+// rotation costs two fp32 products and one add per element and no exchange.
 //
 // Quantisation ([FA3-V3] §4.3 per-block scales; the reading taken is
 // symmetric absmax with no offset): the block's absmax is reduced across the
@@ -49,7 +52,7 @@ __device__ inline float quad_xor(float x) {
 template <typename T, int D, bool ROT, bool QUANT, bool ROPE>
 __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
   constexpr int CPL = D / 4;          // channels per lane
-  constexpr int NV = CPL / 8;         // 16-byte loads per lane
+  constexpr int NV = CPL / 8;         // 16-byte chunks per lane: chunk 4v + li holds y[8v .. 8v+7]
   __shared__ float red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -58,15 +61,16 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
   const int h = (blockIdx.x / p.nblk) % p.H;
   const int b = blockIdx.x / (p.nblk * p.H);
   const long long rs = (long long)p.H * D;     // elements between positions
-  const long long base = ((long long)b * p.N * p.H + h) * D + CPL * li;
+  const long long base = ((long long)b * p.N * p.H + h) * D + 8 * li;
   const int row = blk * 64 + wave * 16 + (lane >> 2);
   const bool valid = row < p.N;
+  // channel of element j: 32·(j/8) + 8·li + j%8
 
   float y[CPL];
   {
     u32x4 raw[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) raw[v] = valid ? *(const u32x4*)(p.x + base + row * rs + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < NV; ++v) raw[v] = valid ? *(const u32x4*)(p.x + base + row * rs + 32 * v) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       const uint32_t w = raw[e / 8][(e % 8) / 2];
@@ -74,31 +78,33 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
     }
   }
   if (ROPE) {
-    // lanes 0, 1 of a quad hold channels [0, d/2), lanes 2, 3 their partners
-    const long long t = (long long)min(row, p.N - 1) * (D / 2) + CPL * (li & 1);
-    float c[CPL], sn[CPL];
+    // elements j < CPL/2 hold channels of [0, d/2) and j + CPL/2 their partners i + d/2;
+    // the table column of element j (and j + CPL/2) is 32·(j/8) + 8·li + j%8
+    const long long t = (long long)min(row, p.N - 1) * (D / 2) + 8 * li;
+    float c[CPL / 2], sn[CPL / 2];
 #pragma unroll
-    for (int v = 0; v < CPL / 4; ++v) {
-      const f32x4 cv = *(const f32x4*)(p.rcos + t + 4 * v);
-      const f32x4 sv = *(const f32x4*)(p.rsin + t + 4 * v);
+    for (int v = 0; v < NV / 2; ++v)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[4 * v + e] = cv[e];
-        sn[4 * v + e] = sv[e];
+      for (int hf = 0; hf < 2; ++hf) {
+        const f32x4 cv = *(const f32x4*)(p.rcos + t + 32 * v + 4 * hf);
+        const f32x4 sv = *(const f32x4*)(p.rsin + t + 32 * v + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[8 * v + 4 * hf + e] = cv[e];
+          sn[8 * v + 4 * hf + e] = sv[e];
+        }
       }
-    }
-    const bool second = (li & 2) != 0;
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      const float other = quad_xor<2>(y[e]);
-      const float a = y[e] * c[e], b = other * sn[e];
-      y[e] = second ? a + b : a - b;
+    for (int j = 0; j < CPL / 2; ++j) {
+      const float x0 = y[j], x1 = y[j + CPL / 2];
+      y[j] = x0 * c[j] - x1 * sn[j];
+      y[j + CPL / 2] = x1 * c[j] + x0 * sn[j];
     }
   }
   if (ROT) {
 #pragma unroll
     for (int e = 0; e < CPL; ++e)
-      if (p.signs[CPL * li + e] < 0) y[e] = -y[e];
+      if (p.signs[32 * (e / 8) + 8 * li + (e % 8)] < 0) y[e] = -y[e];
 #pragma unroll
     for (int hd = 1; hd < CPL; hd *= 2)
 #pragma unroll
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack2<T>(y[8 * v + 2 * e], y[8 * v + 2 * e + 1]);
-        *(u32x4*)((uint16_t*)p.y + base + row * rs + 8 * v) = w;
+        *(u32x4*)((uint16_t*)p.y + base + row * rs + 32 * v) = w;
       }
     }
   } else {
@@ -167,9 +173,10 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
         word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
         w[q] = (uint32_t)word;
       }
+      // chunk 4v + li of the row: 8 code bytes at byte 8·(4v + li)
       uint8_t* dst = (uint8_t*)p.y + base + row * rs;
 #pragma unroll
-      for (int v = 0; v < CPL / 16; ++v) *(u32x4*)(dst + 16 * v) = u32x4{w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]};
+      for (int v = 0; v < NV; ++v) *(u32x2*)(dst + 32 * v) = u32x2{w[2 * v], w[2 * v + 1]};
     }
   }
 }
