@@ -42,11 +42,14 @@ VARIANTS = {
 ARITH_VARIANTS = {"foldscale"}
 # Variants of the fp8 kernel (attn_fwd_fp8.hip rebuilt, libtattn_<name>.so): part of
 # every 8 exponentials of a full tile on the VALU pipe (exp2_valu) instead of
-# v_exp_f32.  The shipped library computes all of them with v_exp_f32.
+# v_exp_f32, or the LDS operand reads issued 3 or 4 products ahead instead of 2.
+# The shipped library computes every exponential with v_exp_f32 and reads 2 ahead.
 FP8_VARIANTS = {
     "fp8_expvalu1": ["-DTATTN_FP8_EXP_VALU=1"],
     "fp8_expvalu2": ["-DTATTN_FP8_EXP_VALU=2"],
     "fp8_expvalu4": ["-DTATTN_FP8_EXP_VALU=4"],
+    "fp8_readahead3": ["-DTATTN_FP8_READ_AHEAD=3"],
+    "fp8_readahead4": ["-DTATTN_FP8_READ_AHEAD=4"],
 }
 
 

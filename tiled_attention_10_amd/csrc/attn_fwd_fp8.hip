@@ -44,7 +44,10 @@ constexpr float kHeadroomLog2 = 8.0f;
 // headroom, p̃ <= 2^(8 + kMaxSlack) = 445.7 < 448, the largest E4M3 value.
 constexpr float kMaxSlack = 0.8f;
 constexpr int kMaxBlocks = 4096;         // scale blocks per head staged in LDS (N <= 262144)
-constexpr int kReadAhead = 2;            // products between an LDS read and its use
+#ifndef TATTN_FP8_READ_AHEAD
+#define TATTN_FP8_READ_AHEAD 2
+#endif
+constexpr int kReadAhead = TATTN_FP8_READ_AHEAD;   // products between an LDS read and its use
 // Of every 8 probabilities of a full tile, how many are computed on the ordinary
 // VALU pipe (exp2_valu) instead of by v_exp_f32, so that the two pipes share the
 // exponentials; tiles with masked keys use v_exp_f32 only.

@@ -10,6 +10,12 @@
         bench.py launches each workload's kernel as one block, so a block separates
         one leg of the benchmark from the others that use the same kernel instance.
 
+    python -m tiled_attention_10_amd.profiling counters DIR [DIR ...]
+        SQ counter summary of the attention kernels from rocprofv3 --pmc runs of the
+        same command (``*_counter_collection.csv``; each directory one pass): the
+        longest dispatch of each kernel, matrix-core busy share, LDS bank-conflict
+        share, VALU and transcendental instructions per MFMA, and the raw values.
+
     python -m tiled_attention_10_amd.profiling traffic --fetch DIR --write DIR
             --copy-fetch DIR --copy-write DIR --workload NAME [--record]
         HBM bytes per dispatch of each attention kernel from two counter runs
@@ -92,6 +98,39 @@ def counter_means(directory: str, counter: str) -> dict:
     return {k: (sum(v) / len(v), len(v)) for k, v in per.items()}
 
 
+def counters(directories) -> str:
+    """Markdown summary of the longest dispatch of each attention kernel (the benchmarked
+    workload's, where a run also launches the kernel on smaller ones) over the counter passes."""
+    vals = {}
+    for d in directories:
+        per = {}
+        for r in csv.DictReader(open(_one(d, "counter_collection.csv"))):
+            name = short_name(r["Kernel_Name"])
+            if not name.startswith("attn_"):
+                continue
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            cv = per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), [dur, {}])[1]
+            cv[r["Counter_Name"]] = cv.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for name, disp in per.items():
+            vals.setdefault(name, {}).update(max(disp.values(), key=lambda x: x[0])[1])
+    out = ["| kernel | XCD active cycles | MFMA busy | LDS bank-conflict cycles / LDS active cycles | "
+           "non-MFMA VALU instructions per MFMA | transcendental per MFMA | SQ_WAVES |", "|---|---|---|---|---|---|---|"]
+    for name, v in vals.items():
+        xcd = v.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / (xcd * 1024)
+        conf = v.get("SQ_LDS_BANK_CONFLICT", float("nan")) / v.get("SQ_LDS_IDX_ACTIVE", float("nan"))
+        mf = v.get("SQ_INSTS_MFMA", float("nan"))
+        valu = (v.get("SQ_INSTS_VALU", float("nan")) - mf) / mf
+        trans = v.get("SQ_INSTS_VALU_TRANS_F32", float("nan")) / mf
+        out.append(f"| {name} | {xcd:.4g} | {100 * busy:.1f} % | {100 * conf:.2f} % | {valu:.2f} | {trans:.2f} | "
+                   f"{v.get('SQ_WAVES', float('nan')):.0f} |")
+    names = list(vals)
+    out += ["", "| counter | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for c in sorted({c for v in vals.values() for c in v}):
+        out.append(f"| {c} | " + " | ".join(f"{vals[n].get(c, float('nan')):.4g}" for n in names) + " |")
+    return "\n".join(out)
+
+
 def copy_factor(directory: str, counter: str) -> float:
     """Counter KiB per KiB actually moved, from the copy calibration run (the dispatch with
     the largest count is the 1 GiB copy)."""
@@ -130,6 +169,8 @@ def main(argv=None) -> None:
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
     b = sub.add_parser("blocks")
     b.add_argument("dir")
     b.add_argument("--kernel", default=None)
@@ -141,6 +182,9 @@ def main(argv=None) -> None:
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(stats(args.dir))
+        return
+    if args.cmd == "counters":
+        print(counters(args.dirs))
         return
     if args.cmd == "blocks":
         print(blocks(args.dir, args.kernel, args.min_calls))
