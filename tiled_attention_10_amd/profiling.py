@@ -161,6 +161,17 @@ def traffic(fetch: str, write: str, copy_fetch: str, copy_write: str, workload: 
                                       "fetch_kib_raw": round(fm[fkn][0], 1), "write_kib_raw": round(wm[wkn][0], 1),
                                       "fetch_bytes": int(fb), "write_bytes": int(wb), "traffic_bytes": int(fb + wb),
                                       "dispatches": [fm[fkn][1], wm[wkn][1]]}
+        if kernel == "attn_decode_split_kernel":
+            # a decode step is the split kernel and its merge kernel: record the step's bytes
+            mf = [k for k in fm if "::attn_decode_merge_kernel<" in k]
+            mw = [k for k in wm if "::attn_decode_merge_kernel<" in k]
+            if mf and mw:
+                mfb, mwb = fm[mf[0]][0] / ff * 1024, wm[mw[0]][0] / wf * 1024
+                e = out[f"{kernel}:{workload}"]
+                e["scope"] = "one decode step: attn_decode_split_kernel + attn_decode_merge_kernel"
+                e["merge_fetch_kib_raw"], e["merge_write_kib_raw"] = round(fm[mf[0]][0], 1), round(wm[mw[0]][0], 1)
+                e["fetch_bytes"], e["write_bytes"] = int(fb + mfb), int(wb + mwb)
+                e["traffic_bytes"] = int(fb + mfb + wb + mwb)
     return out
 
 
