@@ -165,22 +165,25 @@ def launch_stats(torch, fn, n, stream):
 
 
 def fp8_inputs(T, torch, W, w, q, k, v, dev):
+    """E4M3 inputs of the fp8 leg, made by the one-launch prologue, and the prologue variants
+    to time: (inputs, prologue, (with the rotary embedding, embedding as a pass of its own,
+    the plain prologue as three calls))."""
     signs = torch.from_numpy(W.rotation_signs(w.wid, w.d)).to(dev)
-    q8, sq = T.hadamard_rotate(q, signs, quantize=True)
-    k8, sk = T.hadamard_rotate(k, signs, quantize=True)
-    v8, sv = T.hadamard_rotate(v, None, quantize=True)
+    ins = T.fp8_prologue(q, k, v, signs)
+    q8, k8, v8, sq, sk, sv = ins
 
     def prologue():
-        T.hadamard_rotate(q, signs, quantize=True, out=q8, scales=sq)
-        T.hadamard_rotate(k, signs, quantize=True, out=k8, scales=sk)
-        T.hadamard_rotate(v, None, quantize=True, out=v8, scales=sv)
+        T.fp8_prologue(q, k, v, signs, out=ins)
 
     cos, sin = (torch.from_numpy(t).to(dev) for t in W.rotary_tables(w.wid, q.shape[1], q.shape[3]))
 
     def prologue_rope():
         # the same prologue with the rotary embedding of Q and K fused in
-        T.rope_hadamard_rotate(q, cos, sin, signs, quantize=True, out=q8, scales=sq)
-        T.rope_hadamard_rotate(k, cos, sin, signs, quantize=True, out=k8, scales=sk)
+        T.fp8_prologue(q, k, v, signs, (cos, sin), out=ins)
+
+    def prologue_three_calls():
+        T.hadamard_rotate(q, signs, quantize=True, out=q8, scales=sq)
+        T.hadamard_rotate(k, signs, quantize=True, out=k8, scales=sk)
         T.hadamard_rotate(v, None, quantize=True, out=v8, scales=sv)
 
     qr, kr = torch.empty_like(q), torch.empty_like(k)
@@ -193,7 +196,7 @@ def fp8_inputs(T, torch, W, w, q, k, v, dev):
         T.hadamard_rotate(kr, signs, quantize=True, out=k8, scales=sk)
         T.hadamard_rotate(v, None, quantize=True, out=v8, scales=sv)
 
-    return (q8, k8, v8, sq, sk, sv), prologue, (prologue_rope, prologue_rope_unfused)
+    return ins, prologue, (prologue_rope, prologue_rope_unfused, prologue_three_calls)
 
 
 def prologue_bytes(q, k, v):
@@ -488,16 +491,17 @@ def main():
     pre = {}
     fp8_leg = args.dtype != "fp8" and not args.no_fp8 and w.d == 128
     if fp8_leg:
-        ins8, prologue8, prologue_rope = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
+        ins8, prologue8, prologue_more = fp8_inputs(T, torch, W, w, qd, kd, vd, dev)
         out8 = torch.empty(out.shape, dtype=torch.bfloat16, device=dev)
         fms, _ = time_launches(torch, lambda: T.attn_fwd_fp8(*ins8, causal=causal, out=out8),
                                args.steps, args.warmup, stream, min_warm_s=0.25)
         pms, _ = time_launches(torch, prologue8, 20, 10, stream, min_warm_s=0.1)
-        prms, _ = time_launches(torch, prologue_rope[0], 20, 10, stream, min_warm_s=0.1)
-        purms, _ = time_launches(torch, prologue_rope[1], 20, 10, stream, min_warm_s=0.1)
+        prms, _ = time_launches(torch, prologue_more[0], 20, 10, stream, min_warm_s=0.1)
+        purms, _ = time_launches(torch, prologue_more[1], 20, 10, stream, min_warm_s=0.1)
+        p3ms, _ = time_launches(torch, prologue_more[2], 20, 10, stream, min_warm_s=0.1)
         pbytes = prologue_bytes(qd, kd, vd)
         pre["fp8_prologue"] = {"ms": round(pms, 4), "with_rope_ms": round(prms, 4),
-                               "with_rope_separate_pass_ms": round(purms, 4),
+                               "with_rope_separate_pass_ms": round(purms, 4), "three_calls_ms": round(p3ms, 4),
                                "hbm_bytes": pbytes, "GB_per_s": round(pbytes / (pms * 1e-3) / 1e9, 1),
                                "with_rope_GB_per_s": round(pbytes / (prms * 1e-3) / 1e9, 1),
                                "frac_of_hbm_8TBps": round(pbytes / (pms * 1e-3) / 8e12, 4)}

@@ -113,10 +113,10 @@ int attn_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
  * of a Hadamard transform and random signs; [FA3-V3] §4.3: per-block scales).
  *
  * For every row r = x[b, n, h, :] of length d:
- *     y = H_d · (s ⊙ r) / sqrt(d)      if signs != NULL (Sylvester H_d; the
- *                                      butterfly stages run in fp32 with partner
- *                                      distance 1, 2, 4, ..., d/2, then one fp32
- *                                      multiply by fl32(1/sqrt(d)))
+ *     y = H_d · (s ⊙ r) / sqrt(d)      if signs != NULL (Sylvester H_d, as one
+ *                                      butterfly stage per channel-index bit in
+ *                                      fp32, the kernel's order of the stages,
+ *                                      then one fp32 multiply by fl32(1/sqrt(d)))
  *     y = r                            if signs == NULL
  * If scales_out == NULL, y is written to ``y`` in in_dtype (round to nearest
  * even).  Otherwise, per (b, h, block of 64 consecutive rows):
@@ -157,6 +157,31 @@ int hadamard_rotate(const void* x, void* y, const int8_t* signs, float* scales_o
 int rope_hadamard_rotate(const void* x, void* y, const float* rope_cos, const float* rope_sin,
                          const int8_t* signs, float* scales_out, int B, int N, int H, int d,
                          int in_dtype, void* stream);
+
+/*
+ * fp8_prologue — the whole FP8 prologue of one attention call in one launch
+ * ([FA3-card] "低精度优化": incoherent processing of Q and K, fusable with the
+ * rotary embedding; [FA3-V3] §4.3: block quantisation of Q, K and V):
+ *     q8, q_scale = rope_hadamard_rotate(q) or hadamard_rotate(q) with signs, quantised
+ *     k8, k_scale = the same for k, with the same signs and tables
+ *     v8, v_scale = hadamard_rotate(v, signs = NULL), quantised (no rotation, no embedding)
+ * Every output is bit for bit what those separate calls write; one launch
+ * covers all three tensors, so the small K and V passes no longer pay their own
+ * launch and ramp.  The results are the inputs of attn_fwd_fp8().
+ *
+ *   q          [B, N, Hq, d] in_dtype (read);  k, v  [B, N, Hkv, d] (read)
+ *   signs      int8 [d] of +1/-1 for Q and K, or NULL (Q and K only quantised)
+ *   rope_cos, rope_sin   fp32 [N, d/2], both or neither (NULL: no embedding)
+ *   q8, k8, v8           uint8 E4M3FN codes, the layouts of q, k, v (written)
+ *   q_scale    fp32 [B, Hq, ceil(N/64)];  k_scale, v_scale  [B, Hkv, ceil(N/64)] (written)
+ *   d ∈ {64, 128}; Hq a multiple of Hkv; tensors and codes 16-byte aligned,
+ *   scales 4-byte aligned, tables 16-byte aligned; outputs must not alias inputs.
+ * Errors as for hadamard_rotate; one table without the other is TATTN_ERR_INVALID_ARG.
+ */
+int fp8_prologue(const void* q, const void* k, const void* v, const int8_t* signs,
+                 const float* rope_cos, const float* rope_sin, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                 float* q_scale, float* k_scale, float* v_scale, int B, int N, int Hq, int Hkv, int d,
+                 int in_dtype, void* stream);
 
 /*
  * attn_decode_fp8kv — one decode step: each sequence's new query token attends

@@ -199,3 +199,20 @@ def test_noalloc_scratch_limit_against_workspace_sizes(L):
     assert 0 < L.attn_decode_fp8kv_workspace_size(4, 131072, 64, 8, 128) <= limit
     decode_noalloc(L, B=64, Nmax=131072, Hq=64, Hkv=8)
     assert b"scratch" in L.tattn_last_error()
+
+
+def prologue(L, q=P, k=P, v=P, signs=P, rc=None, rs=None, q8=P, k8=P, v8=P, sq=P, sk=P, sv=P, B=1, N=100,
+             Hq=4, Hkv=2, d=128, dtype=2):
+    return L.fp8_prologue(q, k, v, signs, rc, rs, q8, k8, v8, sq, sk, sv, B, N, Hq, Hkv, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(v8=None), INVALID), (dict(sk=None), INVALID), (dict(rc=P), INVALID),
+    (dict(rs=P), INVALID), (dict(B=0), INVALID), (dict(Hq=3, Hkv=2), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED), (dict(k=BAD), MISALIGNED), (dict(q8=P + 8), MISALIGNED),
+    (dict(sv=P + 2), MISALIGNED), (dict(rc=P + 4, rs=P), MISALIGNED),
+    (dict(B=1 << 20, N=1 << 20, Hq=64, Hkv=8), INVALID),
+])
+def test_fp8_prologue_rejects(L, kw, status):
+    assert prologue(L, **kw) == status
+    assert L.tattn_last_error() != b""

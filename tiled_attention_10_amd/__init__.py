@@ -13,7 +13,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "attn_decode_fp8kv",
+__all__ = ["attn_fwd", "attn_fwd_fp8", "hadamard_rotate", "rope_hadamard_rotate", "fp8_prologue", "attn_decode_fp8kv",
            "decode_workspace_size", "TattnError", "lib", "LIB_PATH", "TATTN_F16", "TATTN_BF16",
            "use_library", "variant_path", "attn_decode_fp8kv_noalloc", "TATTN_NOALLOC_SCRATCH_BYTES"]
 
@@ -78,6 +78,8 @@ def _declare(L: ctypes.CDLL) -> None:
     L.hadamard_rotate.restype = i
     L.rope_hadamard_rotate.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     L.rope_hadamard_rotate.restype = i
+    L.fp8_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    L.fp8_prologue.restype = i
     L.attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                                      i, i, i, i, i, f, i, vp]
     L.attn_decode_fp8kv.restype = i
@@ -247,6 +249,42 @@ def rope_hadamard_rotate(x, rope_cos, rope_sin, signs=None, quantize: bool = Fal
     _check(lib().rope_hadamard_rotate(_ptr(x), _ptr(out), _ptr(rope_cos), _ptr(rope_sin), _ptr(signs),
                                       _ptr(scales), B, N, H, d, code, _stream(dev)))
     return (out, scales) if quantize else out
+
+
+def fp8_prologue(q, k, v, signs=None, rope=None, out=None):
+    """The FP8 prologue of one attention call in one launch: q [B, N, Hq, d] and k, v
+    [B, N, Hkv, d] (fp16/bf16); Q and K rotated with ``signs`` (int8 [d], None: no rotation)
+    after the rotary embedding ``rope`` = (cos, sin) fp32 [N, d/2] (None: none), and all
+    three block-quantised.  Returns (q8, k8, v8, q_scale, k_scale, v_scale), the arguments
+    of ``attn_fwd_fp8``; ``out`` may give those six tensors to write into."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, N, H, d]")
+    B, N, Hq, d = q.shape
+    if tuple(k.shape) != tuple(v.shape) or k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    Hkv = k.shape[2]
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    code = _dtype_code(q.dtype)
+    if signs is not None and (signs.dtype != torch.int8 or tuple(signs.shape) != (d,)):
+        raise ValueError(f"signs must be int8 [{d}]")
+    rc, rs = (None, None) if rope is None else rope
+    for name, t in (("rope cos", rc), ("rope sin", rs)):
+        if rope is not None and (t.dtype != torch.float32 or tuple(t.shape) != (N, d // 2) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 [{N}, {d // 2}]")
+    dev = _dev(q, k, v, signs, rc, rs)
+    nb = (N + 63) // 64
+    shapes = [((B, N, Hq, d), torch.uint8), ((B, N, Hkv, d), torch.uint8), ((B, N, Hkv, d), torch.uint8),
+              ((B, Hq, nb), torch.float32), ((B, Hkv, nb), torch.float32), ((B, Hkv, nb), torch.float32)]
+    names = ["q8", "k8", "v8", "q_scale", "k_scale", "v_scale"]
+    outs = [None] * 6 if out is None else list(out)
+    if len(outs) != 6:
+        raise ValueError("out must hold six tensors (q8, k8, v8, q_scale, k_scale, v_scale)")
+    outs = [_out(o, shp, dt, dev, n) for o, (shp, dt), n in zip(outs, shapes, names)]
+    _check(lib().fp8_prologue(_ptr(q), _ptr(k), _ptr(v), _ptr(signs), _ptr(rc), _ptr(rs), *(_ptr(o) for o in outs),
+                              B, N, Hq, Hkv, d, code, _stream(dev)))
+    return tuple(outs)
 
 
 def decode_workspace_size(B: int, Nmax: int, Hq: int, Hkv: int, d: int) -> int:

@@ -240,6 +240,33 @@ int rope_hadamard_rotate(const void* x, void* y, const float* rope_cos, const fl
   return rotate_common(x, y, rope_cos, rope_sin, signs, scales_out, B, N, H, d, in_dtype, stream);
 }
 
+int fp8_prologue(const void* q, const void* k, const void* v, const int8_t* signs, const float* rope_cos,
+                 const float* rope_sin, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* q_scale, float* k_scale,
+                 float* v_scale, int B, int N, int Hq, int Hkv, int d, int in_dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !q8 || !k8 || !v8) return fail(TATTN_ERR_INVALID_ARG, "null tensor pointer");
+  if (!q_scale || !k_scale || !v_scale) return fail(TATTN_ERR_INVALID_ARG, "null scale pointer");
+  if (!rope_cos != !rope_sin) return fail(TATTN_ERR_INVALID_ARG, "give both rotary tables or neither");
+  if (int s = check_shape(B, N, Hq, Hkv, d)) return s;
+  if (d != 64 && d != 128) return fail(TATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+  if (in_dtype != TATTN_F16 && in_dtype != TATTN_BF16)
+    return fail(TATTN_ERR_UNSUPPORTED, "in_dtype %d", in_dtype);
+  if ((long long)((N + 63) / 64) * (Hq + 2LL * Hkv) * B > 0x7fffffffLL)
+    return fail(TATTN_ERR_INVALID_ARG, "too many row blocks");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q8, 16) || !aligned(k8, 16) ||
+      !aligned(v8, 16))
+    return fail(TATTN_ERR_MISALIGNED, "tensors and codes must be 16-byte aligned");
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return fail(TATTN_ERR_MISALIGNED, "scales must be 4-byte aligned");
+  if (rope_cos && (!aligned(rope_cos, 16) || !aligned(rope_sin, 16)))
+    return fail(TATTN_ERR_MISALIGNED, "rotary tables must be 16-byte aligned");
+  tattn::PrologueArgs a{};
+  a.q = q; a.k = k; a.v = v; a.signs = signs; a.rope_cos = rope_cos; a.rope_sin = rope_sin;
+  a.q8 = q8; a.k8 = k8; a.v8 = v8; a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
+  a.B = B; a.N = N; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.dtype = in_dtype;
+  return hip_status(tattn::launch_fp8_prologue(a, (hipStream_t)stream), "fp8 prologue launch");
+}
+
 size_t attn_decode_fp8kv_workspace_size(int B, int Nmax, int Hq, int Hkv, int d) {
   if (B < 1 || Nmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || d != 128) return 0;
   if (too_large(B, Nmax, Hq, d) || too_large(B, Nmax, Hkv, d)) return 0;

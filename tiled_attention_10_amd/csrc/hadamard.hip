@@ -49,17 +49,19 @@ __device__ inline float quad_xor(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
 }
 
+// One (batch, head, 64-row block) of one tensor, block index ``bid`` in
+// (batch, head, block) order, by the 256 threads of a workgroup; ``red`` is 4
+// floats of LDS.
 template <typename T, int D, bool ROT, bool QUANT, bool ROPE>
-__global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
+__device__ inline void rotate_block(const RotParams& p, int bid, float* red) {
   constexpr int CPL = D / 4;          // channels per lane
   constexpr int NV = CPL / 8;         // 16-byte chunks per lane: chunk 4v + li holds y[8v .. 8v+7]
-  __shared__ float red[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 3;
-  const int blk = blockIdx.x % p.nblk;
-  const int h = (blockIdx.x / p.nblk) % p.H;
-  const int b = blockIdx.x / (p.nblk * p.H);
+  const int blk = bid % p.nblk;
+  const int h = (bid / p.nblk) % p.H;
+  const int b = bid / (p.nblk * p.H);
   const long long rs = (long long)p.H * D;     // elements between positions
   const long long base = ((long long)b * p.N * p.H + h) * D + 8 * li;
   const int row = blk * 64 + wave * 16 + (lane >> 2);
@@ -181,6 +183,30 @@ __global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
   }
 }
 
+template <typename T, int D, bool ROT, bool QUANT, bool ROPE>
+__global__ __launch_bounds__(256) void hadamard_kernel(RotParams p) {
+  __shared__ float red[4];
+  rotate_block<T, D, ROT, QUANT, ROPE>(p, blockIdx.x, red);
+}
+
+// The FP8 prologue of one attention call in one launch: the first nq workgroups
+// rotate (and embed, with ROPE) and quantise blocks of Q, the next nk those of K,
+// the rest quantise blocks of V.  The tensor is uniform per workgroup, so the
+// branch costs nothing; each block is computed exactly as hadamard_kernel would.
+struct PrologueParams {
+  RotParams q, k, v;
+  int nq, nk;
+};
+
+template <typename T, int D, bool ROT, bool ROPE>
+__global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
+  __shared__ float red[4];
+  const int bid = blockIdx.x;
+  if (bid < p.nq) rotate_block<T, D, ROT, true, ROPE>(p.q, bid, red);
+  else if (bid < p.nq + p.nk) rotate_block<T, D, ROT, true, ROPE>(p.k, bid - p.nq, red);
+  else rotate_block<T, D, false, true, false>(p.v, bid - p.nq - p.nk, red);
+}
+
 template <typename T, int D, bool ROPE>
 hipError_t launch_dr(const RotParams& p, dim3 grid, bool rot, bool q, hipStream_t stream) {
   const dim3 block(256);
@@ -214,10 +240,52 @@ hipError_t launch_t(const RotateArgs& a, hipStream_t s) {
   return a.d == 128 ? launch_d<T, 128>(a, s) : launch_d<T, 64>(a, s);
 }
 
+RotParams rot_params(const void* x, void* y, const int8_t* signs, float* scales, const float* rcos,
+                     const float* rsin, int N, int H) {
+  RotParams r;
+  r.x = (const uint16_t*)x;
+  r.y = y;
+  r.signs = signs;
+  r.scales = scales;
+  r.rcos = rcos;
+  r.rsin = rsin;
+  r.N = N;
+  r.H = H;
+  r.nblk = (N + 63) / 64;
+  return r;
+}
+
+template <typename T, int D>
+hipError_t launch_prologue_d(const PrologueArgs& a, hipStream_t stream) {
+  PrologueParams p;
+  p.q = rot_params(a.q, a.q8, a.signs, a.q_scale, a.rope_cos, a.rope_sin, a.N, a.Hq);
+  p.k = rot_params(a.k, a.k8, a.signs, a.k_scale, a.rope_cos, a.rope_sin, a.N, a.Hkv);
+  p.v = rot_params(a.v, a.v8, nullptr, a.v_scale, nullptr, nullptr, a.N, a.Hkv);
+  const long long nblk = (a.N + 63) / 64;
+  p.nq = (int)(nblk * a.Hq * a.B);
+  p.nk = (int)(nblk * a.Hkv * a.B);
+  const dim3 grid((unsigned)(p.nq + 2LL * p.nk)), block(256);
+  const bool rot = a.signs != nullptr, rope = a.rope_cos != nullptr;
+  if (rot && rope) hipLaunchKernelGGL((prologue_kernel<T, D, true, true>), grid, block, 0, stream, p);
+  else if (rot) hipLaunchKernelGGL((prologue_kernel<T, D, true, false>), grid, block, 0, stream, p);
+  else if (rope) hipLaunchKernelGGL((prologue_kernel<T, D, false, true>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((prologue_kernel<T, D, false, false>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_prologue_t(const PrologueArgs& a, hipStream_t s) {
+  return a.d == 128 ? launch_prologue_d<T, 128>(a, s) : launch_prologue_d<T, 64>(a, s);
+}
+
 }  // namespace
 
 hipError_t launch_hadamard_rotate(const RotateArgs& a, hipStream_t stream) {
   return a.dtype == TATTN_BF16 ? launch_t<Bf16>(a, stream) : launch_t<F16>(a, stream);
+}
+
+hipError_t launch_fp8_prologue(const PrologueArgs& a, hipStream_t stream) {
+  return a.dtype == TATTN_BF16 ? launch_prologue_t<Bf16>(a, stream) : launch_prologue_t<F16>(a, stream);
 }
 
 }  // namespace tattn

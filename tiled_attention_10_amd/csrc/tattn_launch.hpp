@@ -33,6 +33,25 @@ struct RotateArgs {
   int dtype;
 };
 
+// FP8 prologue of one attention call: Q and K rotated (and embedded) and quantised,
+// V quantised, in one launch.
+struct PrologueArgs {
+  const void* q;            // [B, N, Hq, d] 16-bit
+  const void* k;            // [B, N, Hkv, d]
+  const void* v;
+  const int8_t* signs;      // [d] or NULL (no rotation)
+  const float* rope_cos;    // [N, d/2] or NULL (no rotary embedding)
+  const float* rope_sin;
+  uint8_t* q8;              // E4M3 codes, same layouts
+  uint8_t* k8;
+  uint8_t* v8;
+  float* q_scale;           // [B, H, ceil(N/64)]
+  float* k_scale;
+  float* v_scale;
+  int B, N, Hq, Hkv, d;
+  int dtype;
+};
+
 // Decode step over an FP8 block-quantised KV cache.
 struct DecodeArgs {
   const void* q;            // [B, Hq, d] 16-bit
@@ -68,6 +87,7 @@ int device_cu_count();
 hipError_t launch_attn_fwd16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_fp8(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_hadamard_rotate(const RotateArgs& a, hipStream_t stream);
+hipError_t launch_fp8_prologue(const PrologueArgs& a, hipStream_t stream);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace tattn
