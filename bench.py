@@ -39,6 +39,10 @@ next to bf16 on the same inputs), with ms, TFLOPS and fraction of peak.
 shipped library and every variant, interleaved over rounds, and prints one JSON
 line with each variant's median time and its change against the shipped build.
 
+--sweep times the bf16 kernel (both masks) and the fp8 kernel over a list of
+shapes (sequence lengths 2k to 128k, GQA and MHA, d = 64 and 128) and prints one
+JSON line.
+
 --copy-calibration runs only a plain device copy of known size (for scaling
 the FETCH_SIZE / WRITE_SIZE counters of a profiler run) and exits.
 """
@@ -82,6 +86,8 @@ def parse():
     ap.add_argument("--variant", default=None, help="time a scheduling variant of the library instead")
     ap.add_argument("--ablation", action="store_true", help="time the shipped library against every variant")
     ap.add_argument("--rounds", type=int, default=4, help="interleaved rounds of --ablation")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the 16-bit and fp8 kernels over a list of shapes (one JSON line) and exit")
     return ap.parse_args()
 
 
@@ -389,6 +395,38 @@ def config_legs(T, torch, W, stream, dev, steps=20, warmup=10, min_warm_s=0.25):
     return out
 
 
+SWEEP_SHAPES = [  # B, N, Hq, Hkv, d
+    (16, 2048, 64, 8, 128), (8, 4096, 64, 8, 128), (1, 8192, 64, 8, 128), (1, 16384, 64, 8, 128),
+    (1, 32768, 32, 4, 128), (1, 131072, 8, 1, 128), (4, 8192, 32, 32, 128), (1, 8192, 64, 8, 64),
+]
+
+
+def sweep(args, T, torch, W, stream, dev):
+    """TFLOPS of the bf16 kernel (non-causal and causal) and of the fp8 kernel on E4M3 codes from
+    the one-launch prologue with seeded signs, over SWEEP_SHAPES; each timing is the mean of
+    ``steps`` launches after at least ``warmup`` launches and 0.25 s of them."""
+    out = []
+    for (B, N, Hq, Hkv, d) in SWEEP_SHAPES:
+        q, k, v = (W.to_torch(x, "bf16").to(dev) for x in W.random_qkv(1000 + N + d, B, N, Hq, Hkv, d))
+        o = torch.empty_like(q)
+        row = {"B": B, "N": N, "Hq": Hq, "Hkv": Hkv, "d": d}
+        for causal in (False, True):
+            fl = 4.0 * N * N * d * Hq * B / (2 if causal else 1)
+            ms, _ = time_launches(torch, lambda: T.attn_fwd(q, k, v, causal=causal, out=o), args.steps,
+                                  args.warmup, stream, min_warm_s=0.25)
+            row["bf16_causal" if causal else "bf16"] = _tf(fl, ms)
+            if d == 128:
+                ins = T.fp8_prologue(q, k, v, torch.from_numpy(W.rotation_signs(N, d)).to(dev))
+                ms8, _ = time_launches(torch, lambda: T.attn_fwd_fp8(*ins, causal=causal, out=o), args.steps,
+                                       args.warmup, stream, min_warm_s=0.25)
+                row["fp8_causal" if causal else "fp8"] = _tf(fl, ms8)
+        print(f"[sweep] {row}", file=sys.stderr, flush=True)
+        out.append(row)
+        del q, k, v, o
+    return {"metric": "attention fwd TFLOPS over shapes (4·N²·d·H, causal/2)", "unit": "TFLOPS", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "shapes": out}
+
+
 def ablation(args, T, torch, W, stream, dev):
     """The workload timed with the shipped library and each scheduling variant, in
     interleaved rounds (shipped, v1, v2, ..., shipped, v1, ...), median over rounds."""
@@ -443,6 +481,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     if args.ablation:
         print(json.dumps(ablation(args, T, torch, W, stream, dev)), flush=True)
+        return
+    if args.sweep:
+        print(json.dumps(sweep(args, T, torch, W, stream, dev)), flush=True)
         return
     if args.variant is not None:
         # every call below goes through the variant build of the library

@@ -326,3 +326,20 @@ def test_fp8_variant_within_derived_bound(variant):
             print(f"{variant} causal={causal}: RMSE gpu {e_gpu:.4e}, emulation {e_emul:.4e}")
             assert np.isfinite(o).all() and e_gpu <= rmse_bound(e_emul)
             check_derived(o, (q8, k8, v8, sq, sk, sv), causal, lse=lse)
+
+
+@pytest.mark.parametrize("variant", ["fp8_readahead3", "fp8_readahead4"])
+def test_fp8_read_ahead_variants_bitwise_equal_shipped(variant):
+    # Reading the LDS operands 3 or 4 products ahead instead of 2 changes only when
+    # the reads are issued, not the arithmetic, so the outputs must be bit-identical;
+    # a read racing the ring's loads or the barrier would show up as a difference.
+    for (B, N, Hq, Hkv, seed) in ((1, 1000, 8, 2, 91), (1, 8192, 64, 8, 92), (2, 1100, 96, 8, 93)):
+        q, k, v = (W.to_torch(x, "bf16").to(DEV) for x in W.random_qkv(seed, B, N, Hq, Hkv, 128))
+        ins = T.fp8_prologue(q, k, v, torch.from_numpy(W.rotation_signs(seed, 128)).to(DEV))
+        for causal in (False, True):
+            print(f"[attn_fwd_fp8 {variant}] {(B, N, Hq, Hkv)} causal={causal}", flush=True)
+            o1, l1 = T.attn_fwd_fp8(*ins, causal=causal, return_lse=True)
+            with T.use_library(T.variant_path(variant)):
+                o2, l2 = T.attn_fwd_fp8(*ins, causal=causal, return_lse=True)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
