@@ -4,8 +4,11 @@
  * C ABI.  Plain pointers and sizes only.  Every tensor is a dense row-major
  * array laid out [B, N, H, d] (batch, sequence position, head, channel) in
  * device memory that the caller allocates and owns; the library allocates
- * nothing, and its only global state is a per-device cache of the compute-unit
- * count (written atomically), so calls from several host threads are safe.
+ * nothing.  Its global state is a per-device cache of the compute-unit count
+ * (written atomically) and, for attn_decode_fp8kv_noalloc only, a fixed device
+ * array per GPU with its address (looked up under a lock), so calls from
+ * several host threads are safe (except overlapping attn_decode_fp8kv_noalloc
+ * calls on one GPU, which share that array).
  * Every call is asynchronous on ``stream`` (a hipStream_t; NULL means the
  * default stream) and returns before the GPU has finished.  The attention
  * kernels launch one workgroup per compute unit of the current device and each
@@ -73,6 +76,11 @@ enum {
  *   the fp8 path), else TATTN_ERR_INVALID_ARG.
  *   softmax_scale: finite and > 0 (1/sqrt(d) for the standard definition).
  *   causal: 0 or 1.  dtype: TATTN_F16 or TATTN_BF16 (output in the same type).
+ * Precision: the scores are the exact products of the 16-bit inputs summed in
+ * fp32, times scale·log2(e) in fp32 (one fused multiply-add with the reference
+ * max); each probability is rounded to dtype for P·V, and the denominator sums
+ * the same rounded probabilities, so O is a weighted mean of V rows with fp32
+ * accumulation, rounded once to dtype.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int N, int Hq, int Hkv, int d, float softmax_scale, int causal,
