@@ -117,7 +117,7 @@ def sample_rows(N, seed, n=160, bm=128):
 
 
 @pytest.mark.parametrize("name,causal", [("gqa_bf16_h64kv8_n8192", True), ("gqa_bf16_h64kv8_n8192", False),
-                                         ("long_bf16_h8kv1_n131072", True)])
+                                         ("long_bf16_h8kv1_n131072", True), ("long_bf16_h8kv1_n131072", False)])
 def test_large_workloads_sampled_rows(name, causal):
     w = W.WORKLOADS[name]
     q, k, v = (W.to_torch(x, "bf16") for x in W.qkv_f32(w))
