@@ -13,7 +13,12 @@
  * default stream) and returns before the GPU has finished.  The attention
  * kernels launch one workgroup per compute unit of the current device and each
  * workgroup walks a fixed share of the work; running them beside other kernels
- * on the same device is correct but may serialise part of the grid.
+ * on the same device is correct but may serialise part of the grid.  A call
+ * only launches kernels on ``stream`` (no allocation, copy, memset or
+ * synchronisation), so it can be recorded into a HIP graph by stream capture;
+ * the launch configuration depends on the sizes alone, so a captured call stays
+ * valid for new contents of the same buffers (for the decode step, new sequence
+ * lengths included).
  *
  * Return value: TATTN_OK (0) or one of the TATTN_ERR_* codes below.  Argument
  * checks run on the host before any HIP call, so a rejected call touches
