@@ -15,8 +15,10 @@
  * workgroup walks a fixed share of the work; running them beside other kernels
  * on the same device is correct but may serialise part of the grid.  A call
  * only launches kernels on ``stream`` (no allocation, copy, memset or
- * synchronisation), so it can be recorded into a HIP graph by stream capture;
- * the launch configuration depends on the sizes alone, so a captured call stays
+ * synchronisation), so it can be recorded into a HIP graph by stream capture
+ * (make one call on the device first: the first call per device queries the
+ * compute-unit count and, for the allocation-free entry point, the scratch
+ * address); the launch configuration depends on the sizes alone, so a captured call stays
  * valid for new contents of the same buffers (for the decode step, new sequence
  * lengths included).
  *
